@@ -1,0 +1,225 @@
+// Host side of libmla_decode: argument checks, launch planning, workspace
+// layout and the kernel launches of one decode call.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mla_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Largest cache length the selection bitmap supports (LDS holds L_max/8 bytes).
+constexpr int kMaxCacheLen = 1 << 20;
+constexpr int kMaxBatch = 1 << 20;
+constexpr int kMaxHeads = 1 << 12;
+constexpr int kMaxSplits = 64;
+
+int query_num_cus(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    *out = n;
+    return 0;
+}
+
+// Split-KV plan.  The attention grid is B * hgroups * splits workgroups of
+// one per CU (the kernel uses all of a CU's registers); splits fill the
+// chip when B * hgroups is below the CU count, each keeping at least two
+// tiles of work.
+bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_splits, mla::Plan* pl) {
+    if (B < 1 || H < 1 || K < 1 || num_cus < 1) return false;
+    pl->bf16_path = dtype_act == MLA_DTYPE_BF16;
+    if (!pl->bf16_path) {
+        pl->nhg = 0; pl->heads_per_wg = 1; pl->hgroups = H; pl->splits = 1; pl->tile_rows = 256;
+        return forced_splits <= 1;
+    }
+    const int need = (H + 31) / 32;
+    pl->nhg = need >= 2 ? 2 : 1;                    // groups of 32 heads per workgroup
+    pl->heads_per_wg = 32 * pl->nhg;
+    pl->hgroups = (H + pl->heads_per_wg - 1) / pl->heads_per_wg;
+    pl->tile_rows = pl->nhg == 4 ? 32 : 64;
+    int S;
+    if (forced_splits > 0) {
+        S = forced_splits;
+    } else {
+        const int base = B * pl->hgroups;
+        S = base >= num_cus ? 1 : num_cus / base;
+        const int max_by_rows = (K + 2 * pl->tile_rows - 1) / (2 * pl->tile_rows);
+        if (S > max_by_rows) S = max_by_rows;
+        if (S < 1) S = 1;
+    }
+    if (S > kMaxSplits) return false;
+    pl->splits = S;
+    return true;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace mla {
+
+size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* base, Work* w) {
+    const size_t act = bf16_path ? 2 : 4;
+    size_t off = 0;
+    char* p = (char*)base;
+    Work ww{};
+    ww.qt = p + off;       off = align256(off + (size_t)B * H * 576 * act);
+    ww.list = (int32_t*)(p + off);  off = align256(off + (size_t)B * K * 4);
+    ww.counts = (int32_t*)(p + off); off = align256(off + (size_t)B * 4);
+    ww.status = (uint32_t*)(p + off); off = align256(off + 4);
+    ww.opart = p + off;
+    off = align256(off + (bf16_path ? (size_t)B * splits * H * 512 * 2 : (size_t)B * H * 512 * 4));
+    ww.lsepart = (float*)(p + off);
+    off = align256(off + (size_t)B * (bf16_path ? splits : 1) * H * 4);
+    ww.bytes = off;
+    if (w) *w = ww;
+    return off;
+}
+
+}  // namespace mla
+
+extern "C" {
+
+const char* mla_last_error(void) { return g_err; }
+
+size_t mla_decode_params_size(void) { return sizeof(mla_decode_params_t); }
+
+double mla_softmax_scale(int qk_head_dim, const mla_rope_cfg_t* cfg) {
+    if (!cfg || qk_head_dim < 1) return -1.0;
+    double s = 1.0 / sqrt((double)qk_head_dim);
+    if (cfg->max_seq_len > cfg->original_seq_len) {
+        const double m = 0.1 * cfg->mscale * log(cfg->factor) + 1.0;
+        s = s * m * m;
+    }
+    return s;
+}
+
+int mla_rope_freqs(const mla_rope_cfg_t* cfg, float* table, void* stream) {
+    g_err[0] = 0;
+    if (!cfg || !table) return fail(MLA_ERR_INVALID_ARG, "mla_rope_freqs: null cfg or table");
+    if (cfg->rope_dim != 64) return fail(MLA_ERR_UNSUPPORTED, "mla_rope_freqs: rope_dim must be 64");
+    if (cfg->max_seq_len < 1 || cfg->original_seq_len < 1 || cfg->reserved != 0)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_freqs: bad lengths");
+    if (!(cfg->theta > 1.0) || !(cfg->factor > 0.0) || !(cfg->beta_fast > 0.0) || !(cfg->beta_slow > 0.0))
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_freqs: theta must exceed 1; factor and betas positive");
+    if (mla::launch_rope_freqs(*cfg, table, (hipStream_t)stream) != hipSuccess)
+        return fail(MLA_ERR_HIP, "mla_rope_freqs: launch failed");
+    return MLA_OK;
+}
+
+int mla_decode_num_splits(int B, int H, int K, int dtype_act, int num_cus) {
+    if (num_cus == 0 && query_num_cus(&num_cus) != 0) return -1;
+    mla::Plan pl;
+    if ((dtype_act != MLA_DTYPE_BF16 && dtype_act != MLA_DTYPE_F32) || !make_plan(B, H, K, dtype_act, num_cus, 0, &pl))
+        return -1;
+    return pl.splits;
+}
+
+size_t mla_decode_workspace_size(int B, int H, int K, int dtype_act, int dtype_w, int num_cus, int num_splits) {
+    if (B < 1 || B > kMaxBatch || H < 1 || H > kMaxHeads || K < 1) return 0;
+    if ((dtype_act != MLA_DTYPE_BF16 && dtype_act != MLA_DTYPE_F32) ||
+        (dtype_w != MLA_DTYPE_BF16 && dtype_w != MLA_DTYPE_F32))
+        return 0;
+    if (num_cus == 0 && query_num_cus(&num_cus) != 0) return 0;
+    mla::Plan pl;
+    if (!make_plan(B, H, K, dtype_act, num_cus, num_splits, &pl)) return 0;
+    return mla::workspace_layout(B, H, K, pl.bf16_path, pl.splits, nullptr, nullptr);
+}
+
+int mla_decode_attn(mla_decode_params_t* p, void* stream) {
+    g_err[0] = 0;
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "null params");
+    p->validate_status = 0;
+    if (p->d_nope != 128 || p->d_rope != 64 || p->d_v != 128 || p->kv_rank != 512)
+        return fail(MLA_ERR_UNSUPPORTED, "dims must be d_nope=128, d_rope=64, d_v=128, kv_rank=512");
+    auto okdt = [](int d) { return d == MLA_DTYPE_BF16 || d == MLA_DTYPE_F32; };
+    if (!okdt(p->dtype_act) || !okdt(p->dtype_w) || !okdt(p->dtype_out))
+        return fail(MLA_ERR_UNSUPPORTED, "unknown dtype");
+    if (p->B < 1 || p->B > kMaxBatch || p->H < 1 || p->H > kMaxHeads || p->K < 1)
+        return fail(MLA_ERR_INVALID_ARG, "sizes out of range: B=%d H=%d K=%d", p->B, p->H, p->K);
+    if (p->max_cache_len < 1 || p->max_cache_len > kMaxCacheLen)
+        return fail(MLA_ERR_INVALID_ARG, "max_cache_len must be in [1, %d]", kMaxCacheLen);
+    if (p->rope_table_len < 1) return fail(MLA_ERR_INVALID_ARG, "rope_table_len must be >= 1");
+    if (!(p->softmax_scale > 0.f) || !isfinite(p->softmax_scale))
+        return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
+    if (p->num_splits < 0 || p->num_splits > kMaxSplits || p->num_cus < 0)
+        return fail(MLA_ERR_INVALID_ARG, "num_splits must be in [0, %d], num_cus >= 0", kMaxSplits);
+    if (p->flags & ~MLA_FLAG_VALIDATE) return fail(MLA_ERR_INVALID_ARG, "unknown flags");
+    const void* ptrs[] = {p->q_nope, p->q_pe, p->w_uk, p->w_uv, p->kv_cache, p->pe_cache,
+                          p->topk_indices, p->cache_lens, p->rope_table, p->out, p->workspace};
+    const char* names[] = {"q_nope", "q_pe", "w_uk", "w_uv", "kv_cache", "pe_cache",
+                           "topk_indices", "cache_lens", "rope_table", "out", "workspace"};
+    for (int i = 0; i < 11; ++i) {
+        if (!ptrs[i]) return fail(MLA_ERR_INVALID_ARG, "%s is null", names[i]);
+        if (!aligned16(ptrs[i])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
+    }
+    if (p->lse_out && ((uintptr_t)p->lse_out & 3u)) return fail(MLA_ERR_INVALID_ARG, "lse_out misaligned");
+    const int64_t vec_strides[] = {p->q_nope_stride_b, p->q_nope_stride_h, p->w_uv_stride_h,
+                                   p->kv_stride_b, p->kv_stride_t, p->pe_stride_b, p->pe_stride_t};
+    for (int64_t st : vec_strides)
+        if (st < 0 || (st & 7)) return fail(MLA_ERR_INVALID_ARG, "q_nope/w_uv/cache strides must be non-negative multiples of 8");
+    const int64_t other[] = {p->q_pe_stride_b, p->q_pe_stride_h, p->w_uk_stride_h, p->idx_stride_b,
+                             p->out_stride_b, p->out_stride_h};
+    for (int64_t st : other)
+        if (st < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride");
+    if (p->kv_stride_t < 512 || p->pe_stride_t < 64 || p->q_nope_stride_h < 128 || p->q_pe_stride_h < 64 ||
+        p->w_uk_stride_h < 128 * 512 || p->w_uv_stride_h < 128 * 512 || p->idx_stride_b < p->K ||
+        p->out_stride_h < 128)
+        return fail(MLA_ERR_INVALID_ARG, "a stride is smaller than the row it steps over");
+
+    int num_cus = p->num_cus;
+    if (num_cus == 0 && query_num_cus(&num_cus) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
+    mla::Plan plan;
+    if (!make_plan(p->B, p->H, p->K, p->dtype_act, num_cus, p->num_splits, &plan))
+        return fail(MLA_ERR_INVALID_ARG, "no launch plan (fp32 activations take num_splits 0 or 1)");
+    mla::Work w;
+    const size_t need = mla::workspace_layout(p->B, p->H, p->K, plan.bf16_path, plan.splits, p->workspace, &w);
+    if (p->workspace_size < need)
+        return fail(MLA_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", p->workspace_size, need);
+
+    hipStream_t s = (hipStream_t)stream;
+    const bool validate = (p->flags & MLA_FLAG_VALIDATE) != 0;
+    hipEvent_t* ev = (hipEvent_t*)p->profile_events;
+    if (validate && hipMemsetAsync(w.status, 0, 4, s) != hipSuccess)
+        return fail(MLA_ERR_HIP, "hipMemsetAsync failed");
+    hipError_t e;
+    if (ev && hipEventRecord(ev[0], s) != hipSuccess) return fail(MLA_ERR_HIP, "hipEventRecord failed");
+    if ((e = mla::launch_prep(*p, plan, w, validate, s)) != hipSuccess)
+        return fail(MLA_ERR_HIP, "prep launch: %s", hipGetErrorString(e));
+    if (ev && (hipEventRecord(ev[1], s) != hipSuccess || hipEventRecord(ev[2], s) != hipSuccess))
+        return fail(MLA_ERR_HIP, "hipEventRecord failed");
+    if ((e = mla::launch_attn(*p, plan, w, s)) != hipSuccess)
+        return fail(MLA_ERR_HIP, "attention launch: %s", hipGetErrorString(e));
+    if (ev && (hipEventRecord(ev[3], s) != hipSuccess || hipEventRecord(ev[4], s) != hipSuccess))
+        return fail(MLA_ERR_HIP, "hipEventRecord failed");
+    if ((e = mla::launch_merge(*p, plan, w, s)) != hipSuccess)
+        return fail(MLA_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+    if (ev && hipEventRecord(ev[5], s) != hipSuccess) return fail(MLA_ERR_HIP, "hipEventRecord failed");
+    if (validate) {
+        uint32_t st = 0;
+        if (hipMemcpyAsync(&st, w.status, 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return fail(MLA_ERR_HIP, "validation readback failed");
+        p->validate_status = st;
+        if (st) return fail(MLA_ERR_INVALID_INDEX, "invalid selection or cache length (status 0x%x)", st);
+    }
+    return MLA_OK;
+}
+
+}  // extern "C"

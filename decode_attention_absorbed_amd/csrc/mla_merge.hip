@@ -1,0 +1,244 @@
+// Merge of split-KV partials and the W_UV up-projection, plus the fp32
+// attention used when the activations are fp32.
+//
+// Sources (atlas pages on DeepSeek-V3.2-Exp sparse latent attention):
+//   page "Rotated query part", excerpt mla-decode: softmax over the selected
+//   scores, the weighted latent sum and the per-head W_UV up-projection
+//   (x . W_UV[h]^T over the 512 latent columns, 128 outputs per head).
+//   Merging independently normalised partials by their log-sum-exp is the
+//   standard split-softmax identity; the pages do not partition the keys.
+#include "mla_device.hpp"
+#include "mla_internal.hpp"
+
+namespace mla {
+
+// ---------------------------------------------------------------------------
+// bf16 path: out[b, h, :] = W_UV[h] . sum_s w_{b,s} o_s[b, h, :]
+//   w_{b,s} = 2^(lse_s - M) / sum_s' 2^(lse_s' - M),  M = max_s lse_s.
+// Workgroup (head h, output half dh) covers every sequence.  bf16 MFMA with
+// M = sequences (32 per block), N = 64 outputs, K = 512 latent columns split
+// over the 4 waves (128 each) and reduced through LDS.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+    int B, H, S;
+    const bf16* opart;
+    const float* lsepart;
+    const void* w_uv; long long wv_sh;
+    void* out; long long out_sb, out_sh;
+    float* lse_out;
+};
+
+template <typename WT, typename OutT>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+    __shared__ float red[4 * 2 * 16 * 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    // the two output halves of one head sit 8 ids apart (same XCD, shared L2)
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k8 = id >> 3;
+    const int dh = k8 & 1, h = (k8 >> 1) * 8 + xcd;
+    if (h >= a.H) return;
+
+    const WT* W = (const WT*)a.w_uv + h * a.wv_sh;
+    bf16x8 bw[2][8];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const int d = 64 * dh + 32 * nb + l32;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            bw[nb][kb] = load8_bf16<WT>(W + d * RANK + 128 * wave + 16 * kb + 8 * g);
+    }
+
+    for (int b0 = 0; b0 < a.B; b0 += 32) {
+        const int bA = b0 + l32;
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        float M = -INFINITY, Wsum = 0.f;
+        if (bA < a.B) {
+            const float* ls = a.lsepart + (long long)bA * a.S * a.H + h;
+            for (int s = 0; s < a.S; ++s) M = fmaxf(M, ls[(long long)s * a.H]);
+            for (int s = 0; s < a.S; ++s) Wsum += exp2f(ls[(long long)s * a.H] - M);
+            const float invW = 1.f / Wsum;
+            float xs[8][8];
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
+            for (int s = 0; s < a.S; ++s) {
+                const float ws = exp2f(ls[(long long)s * a.H] - M) * invW;
+                const bf16* src = a.opart + (((long long)bA * a.S + s) * a.H + h) * RANK + 128 * wave + 8 * g;
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) {
+                    const bf16x8 v = *(const bf16x8*)(src + 16 * kb);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) xs[kb][j] = fmaf(ws, (float)v[j], xs[kb][j]);
+                }
+            }
+            bf16x8 av[8];
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) av[kb][j] = f2bf(xs[kb][j]);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) acc[nb] = mfma32(av[kb], bw[nb][kb], acc[nb]);
+        } else {
+            bf16x8 av = bf16x8{};
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) acc[nb] = mfma32(av, bw[nb][kb], acc[nb]);
+        }
+        if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
+            a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
+        __syncthreads();                        // previous block's reads of red[] done
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[((wave * 2 + nb) * 16 + i) * 64 + lane] = acc[nb][i];
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = tid + 256 * k;
+            const int dl = e & 63, bl = e >> 6;
+            const int nb = dl >> 5, n = dl & 31;
+            const int i = 4 * (bl >> 3) + (bl & 3), gg = (bl >> 2) & 1;
+            const int ln = gg * 32 + n;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + ln];
+            const int bo = b0 + bl;
+            if (bo < a.B)
+                ((OutT*)a.out)[bo * a.out_sb + h * a.out_sh + 64 * dh + dl] = from_f32<OutT>(v);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path.  attn_f32: one workgroup per (sequence, head); scores, softmax
+// and the weighted latent sum in fp32 over the compacted selection, 256 rows
+// at a time with an online rescale between chunks.  Writes the normalised
+// latent sum (fp32) and the log2-domain sum-exp.
+// ---------------------------------------------------------------------------
+struct AttnF32Args {
+    int B, H, K;
+    float scale;
+    const float* qt;
+    const int32_t* list;
+    const int32_t* counts;
+    const float* kv; long long kv_sb, kv_st;
+    const float* pe; long long pe_sb, pe_st;
+    float* olat;
+    float* lse2;
+};
+
+__global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
+    __shared__ float qs[ROW];
+    __shared__ float ps[256];
+    __shared__ float wred[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
+    const float* q = a.qt + ((long long)b * a.H + h) * ROW;
+    for (int i = tid; i < ROW; i += 256) qs[i] = q[i];
+    __syncthreads();
+    const int cnt = a.counts[b];
+    const int32_t* list = a.list + (long long)b * a.K;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int base = 0; base < cnt; base += 256) {
+        const int j = base + tid;
+        float sc = -INFINITY;
+        if (j < cnt) {
+            const long long t = list[j];
+            const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
+            const float* r = a.pe + b * a.pe_sb + t * a.pe_st;
+            float acc = 0.f;
+            for (int k = 0; k < RANK; ++k) acc = fmaf(qs[k], c[k], acc);
+            for (int k = 0; k < D_ROPE; ++k) acc = fmaf(qs[RANK + k], r[k], acc);
+            sc = acc * a.scale;
+        }
+        float cm = wave_max(sc);
+        if (lane == 0) wred[wave] = cm;
+        __syncthreads();
+        cm = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
+        __syncthreads();
+        const float mn = fmaxf(m, cm);
+        const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
+        const float p = j < cnt ? expf(sc - mn) : 0.f;
+        ps[tid] = p;
+        float psum = wave_sum(p);
+        if (lane == 0) wred[wave] = psum;
+        __syncthreads();
+        psum = wred[0] + wred[1] + wred[2] + wred[3];
+        l = l * alpha + psum;
+        o0 *= alpha;
+        o1 *= alpha;
+        m = mn;
+        const int nrow = min(256, cnt - base);
+        for (int r = 0; r < nrow; ++r) {
+            const long long t = list[base + r];
+            const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
+            const float pr = ps[r];
+            o0 = fmaf(pr, c[tid], o0);
+            o1 = fmaf(pr, c[tid + 256], o1);
+        }
+        __syncthreads();
+    }
+    const float inv = l > 0.f ? 1.f / l : NAN;
+    float* dst = a.olat + ((long long)b * a.H + h) * RANK;
+    dst[tid] = o0 * inv;
+    dst[tid + 256] = o1 * inv;
+    if (tid == 0) a.lse2[(long long)b * a.H + h] = (m + logf(l)) * LOG2E;
+}
+
+// fp32 up-projection: one thread per (sequence, head, output feature).
+template <typename WT, typename OutT>
+__global__ __launch_bounds__(256) void uproj_f32_kernel(MergeArgs a, const float* olat) {
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (long long)a.B * a.H * D_V) return;
+    const int d = (int)(e % D_V), h = (int)((e / D_V) % a.H), b = (int)(e / D_V / a.H);
+    const float* x = olat + ((long long)b * a.H + h) * RANK;
+    const WT* w = (const WT*)a.w_uv + h * a.wv_sh + (long long)d * RANK;
+    float acc = 0.f;
+    for (int c = 0; c < RANK; ++c) acc = fmaf(x[c], to_f32(w[c]), acc);
+    ((OutT*)a.out)[b * a.out_sb + h * a.out_sh + d] = from_f32<OutT>(acc);
+    if (d == 0 && a.lse_out) a.lse_out[(long long)b * a.H + h] = a.lsepart[(long long)b * a.H + h] * LN2;
+}
+
+hipError_t launch_attn_f32(const mla_decode_params_t& p, const Work& w, hipStream_t s) {
+    AttnF32Args a{};
+    a.B = p.B; a.H = p.H; a.K = p.K; a.scale = p.softmax_scale;
+    a.qt = (const float*)w.qt; a.list = w.list; a.counts = w.counts;
+    a.kv = (const float*)p.kv_cache; a.kv_sb = p.kv_stride_b; a.kv_st = p.kv_stride_t;
+    a.pe = (const float*)p.pe_cache; a.pe_sb = p.pe_stride_b; a.pe_st = p.pe_stride_t;
+    a.olat = (float*)w.opart; a.lse2 = w.lsepart;
+    hipLaunchKernelGGL(attn_f32_kernel, dim3(p.B * p.H), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Work& w, hipStream_t s) {
+    MergeArgs a{};
+    a.B = p.B; a.H = p.H; a.S = plan.splits;
+    a.opart = (const bf16*)w.opart; a.lsepart = w.lsepart;
+    a.w_uv = p.w_uv; a.wv_sh = p.w_uv_stride_h;
+    a.out = p.out; a.out_sb = p.out_stride_b; a.out_sh = p.out_stride_h;
+    a.lse_out = p.lse_out;
+    const bool wf = p.dtype_w == MLA_DTYPE_F32, of = p.dtype_out == MLA_DTYPE_F32;
+    if (plan.bf16_path) {
+        const dim3 grid(((p.H + 7) / 8) * 16), block(256);
+        if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), grid, block, 0, s, a);
+        else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), grid, block, 0, s, a);
+        else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), grid, block, 0, s, a);
+    } else {
+        const long long n = (long long)p.B * p.H * D_V;
+        const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+        const float* olat = (const float*)w.opart;
+        if (wf && of) hipLaunchKernelGGL((uproj_f32_kernel<float, float>), grid, block, 0, s, a, olat);
+        else if (wf) hipLaunchKernelGGL((uproj_f32_kernel<float, bf16>), grid, block, 0, s, a, olat);
+        else if (of) hipLaunchKernelGGL((uproj_f32_kernel<bf16, float>), grid, block, 0, s, a, olat);
+        else hipLaunchKernelGGL((uproj_f32_kernel<bf16, bf16>), grid, block, 0, s, a, olat);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,234 @@
+"""ctypes binding of libmla_decode.so (include/mla_decode.h).
+
+Argument marshalling only: tensors are passed by device pointer, strides and
+dtype codes; every step of the decode runs in the library's HIP kernels.
+PyTorch provides device memory and the stream.  There is no fallback: if the
+library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmla_decode.so")
+
+MLA_OK, MLA_ERR_INVALID_ARG, MLA_ERR_UNSUPPORTED, MLA_ERR_WORKSPACE, MLA_ERR_INVALID_INDEX, MLA_ERR_HIP = range(6)
+MLA_DTYPE_F32, MLA_DTYPE_BF16 = 0, 1
+MLA_FLAG_VALIDATE = 1
+MLA_BAD_INDEX_RANGE, MLA_BAD_DUPLICATE, MLA_BAD_EMPTY, MLA_BAD_CACHE_LEN = 1, 2, 4, 8
+MLA_NUM_KERNELS = 3
+KERNEL_NAMES = ("prep", "attention", "merge")
+
+
+class RopeCfg(ctypes.Structure):
+    _fields_ = [("rope_dim", ctypes.c_int32), ("max_seq_len", ctypes.c_int32),
+                ("original_seq_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("theta", ctypes.c_double), ("factor", ctypes.c_double),
+                ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double),
+                ("mscale", ctypes.c_double)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("kv_rank", ctypes.c_int32), ("max_cache_len", ctypes.c_int32),
+                ("rope_table_len", ctypes.c_int32),
+                ("dtype_act", ctypes.c_int32), ("dtype_w", ctypes.c_int32), ("dtype_out", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("softmax_scale", ctypes.c_float),
+                ("q_nope", _P), ("q_nope_stride_b", _I64), ("q_nope_stride_h", _I64),
+                ("q_pe", _P), ("q_pe_stride_b", _I64), ("q_pe_stride_h", _I64),
+                ("w_uk", _P), ("w_uk_stride_h", _I64),
+                ("w_uv", _P), ("w_uv_stride_h", _I64),
+                ("kv_cache", _P), ("kv_stride_b", _I64), ("kv_stride_t", _I64),
+                ("pe_cache", _P), ("pe_stride_b", _I64), ("pe_stride_t", _I64),
+                ("topk_indices", _P), ("idx_stride_b", _I64),
+                ("cache_lens", _P),
+                ("rope_table", _P),
+                ("out", _P), ("out_stride_b", _I64), ("out_stride_h", _I64),
+                ("lse_out", _P),
+                ("workspace", _P), ("workspace_size", ctypes.c_size_t),
+                ("profile_events", _P),
+                ("validate_status", ctypes.c_uint32), ("reserved0", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with decode_attention_absorbed_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        L.mla_rope_freqs.argtypes = [ctypes.POINTER(RopeCfg), _P, _P]
+        L.mla_rope_freqs.restype = ctypes.c_int
+        L.mla_softmax_scale.argtypes = [ctypes.c_int, ctypes.POINTER(RopeCfg)]
+        L.mla_softmax_scale.restype = ctypes.c_double
+        L.mla_decode_num_splits.argtypes = [ctypes.c_int] * 5
+        L.mla_decode_num_splits.restype = ctypes.c_int
+        L.mla_decode_workspace_size.argtypes = [ctypes.c_int] * 7
+        L.mla_decode_workspace_size.restype = ctypes.c_size_t
+        L.mla_decode_attn.argtypes = [ctypes.POINTER(DecodeParams), _P]
+        L.mla_decode_attn.restype = ctypes.c_int
+        L.mla_decode_params_size.argtypes = []
+        L.mla_decode_params_size.restype = ctypes.c_size_t
+        L.mla_last_error.argtypes = []
+        L.mla_last_error.restype = ctypes.c_char_p
+        if L.mla_decode_params_size() != ctypes.sizeof(DecodeParams):
+            raise RuntimeError("mla_decode_params_t layout mismatch between the binding and the library")
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().mla_last_error().decode()
+
+
+class MLAError(RuntimeError):
+    def __init__(self, code, msg, status=0):
+        super().__init__(f"mla error {code}: {msg}")
+        self.code = code
+        self.status = status
+
+
+def rope_cfg(rope: dict) -> RopeCfg:
+    return RopeCfg(rope_dim=int(rope["rope_dim"]), max_seq_len=int(rope["max_seq_len"]),
+                   original_seq_len=int(rope["original_seq_len"]), reserved=0,
+                   theta=float(rope["theta"]), factor=float(rope["factor"]),
+                   beta_fast=float(rope["beta_fast"]), beta_slow=float(rope["beta_slow"]),
+                   mscale=float(rope["mscale"]))
+
+
+def softmax_scale(qk_head_dim: int, rope: dict) -> float:
+    cfg = rope_cfg(rope)
+    return lib().mla_softmax_scale(qk_head_dim, ctypes.byref(cfg))
+
+
+def num_splits(B, H, K, dtype_act, num_cus=0) -> int:
+    return lib().mla_decode_num_splits(B, H, K, dtype_act, num_cus)
+
+
+def workspace_size(B, H, K, dtype_act, dtype_w, num_cus=0, num_splits=0) -> int:
+    return lib().mla_decode_workspace_size(B, H, K, dtype_act, dtype_w, num_cus, num_splits)
+
+
+# ---------------------------------------------------------------------------
+# torch-facing helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return MLA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MLA_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def rope_freqs(rope: dict, table=None, stream=None):
+    """Fill (or allocate) the fp32 [max_seq_len, 32, 2] rotation table."""
+    torch = _torch()
+    if table is None:
+        table = torch.empty((int(rope["max_seq_len"]), int(rope["rope_dim"]) // 2, 2),
+                            dtype=torch.float32, device="cuda")
+    cfg = rope_cfg(rope)
+    rc = lib().mla_rope_freqs(ctypes.byref(cfg), ctypes.c_void_p(table.data_ptr()), _stream_handle(stream))
+    if rc != MLA_OK:
+        raise MLAError(rc, last_error())
+    return table
+
+
+def _inner_contig(name, t, width):
+    if t.shape[-1] != width or t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be {width} and contiguous")
+
+
+def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
+                 softmax_scale, out, lse=None, workspace=None, num_splits=0, num_cus=0, validate=False,
+                 events=None) -> DecodeParams:
+    """Fill mla_decode_params_t from torch tensors (shapes as in the header)."""
+    torch = _torch()
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    K = topk_indices.shape[1]
+    for name, t, w in (("q_nope", q_nope, 128), ("q_pe", q_pe, 64), ("w_uk", w_uk, 512), ("w_uv", w_uv, 512),
+                       ("kv_cache", kv_cache, 512), ("pe_cache", pe_cache, 64), ("out", out, 128)):
+        _inner_contig(name, t, w)
+    if w_uk.stride(1) != 512 or w_uv.stride(1) != 512:
+        raise ValueError("w_uk / w_uv rows must be contiguous [H, 128, 512]")
+    if topk_indices.dtype != torch.int32 or cache_lens.dtype != torch.int32:
+        raise TypeError("topk_indices and cache_lens must be int32")
+    if topk_indices.stride(1) != 1:
+        raise ValueError("topk_indices rows must be contiguous")
+    p = DecodeParams()
+    p.B, p.H, p.K = B, H, K
+    p.d_nope, p.d_rope, p.d_v, p.kv_rank = 128, 64, 128, 512
+    p.max_cache_len = kv_cache.shape[1]
+    p.rope_table_len = rope_table.shape[0]
+    p.dtype_act = _dtype_code(kv_cache)
+    p.dtype_w = _dtype_code(w_uk)
+    p.dtype_out = _dtype_code(out)
+    p.num_cus = num_cus
+    p.num_splits = num_splits
+    p.flags = MLA_FLAG_VALIDATE if validate else 0
+    p.softmax_scale = softmax_scale
+    p.q_nope, p.q_nope_stride_b, p.q_nope_stride_h = q_nope.data_ptr(), q_nope.stride(0), q_nope.stride(1)
+    p.q_pe, p.q_pe_stride_b, p.q_pe_stride_h = q_pe.data_ptr(), q_pe.stride(0), q_pe.stride(1)
+    p.w_uk, p.w_uk_stride_h = w_uk.data_ptr(), w_uk.stride(0)
+    p.w_uv, p.w_uv_stride_h = w_uv.data_ptr(), w_uv.stride(0)
+    p.kv_cache, p.kv_stride_b, p.kv_stride_t = kv_cache.data_ptr(), kv_cache.stride(0), kv_cache.stride(1)
+    p.pe_cache, p.pe_stride_b, p.pe_stride_t = pe_cache.data_ptr(), pe_cache.stride(0), pe_cache.stride(1)
+    p.topk_indices, p.idx_stride_b = topk_indices.data_ptr(), topk_indices.stride(0)
+    p.cache_lens = cache_lens.data_ptr()
+    p.rope_table = rope_table.data_ptr()
+    p.out, p.out_stride_b, p.out_stride_h = out.data_ptr(), out.stride(0), out.stride(1)
+    p.lse_out = lse.data_ptr() if lse is not None else None
+    if workspace is not None:
+        p.workspace, p.workspace_size = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    p.profile_events = events
+    return p
+
+
+def decode_attn(params: DecodeParams, stream=None, check=True) -> int:
+    """Run mla_decode_attn; raises MLAError on a non-zero code when check."""
+    rc = lib().mla_decode_attn(ctypes.byref(params), _stream_handle(stream))
+    if check and rc != MLA_OK:
+        raise MLAError(rc, last_error(), params.validate_status)
+    return rc
+
+
+def decode(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
+           softmax_scale, out=None, lse=None, workspace=None, out_dtype=None, num_splits=0,
+           validate=False, stream=None, with_lse=True):
+    """Allocate what is missing, run one decode step; returns (out, lse)."""
+    torch = _torch()
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    if out is None:
+        out = torch.empty((B, H, 128), dtype=out_dtype or torch.float32, device=q_nope.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    if workspace is None:
+        n = workspace_size(B, H, topk_indices.shape[1], _dtype_code(kv_cache), _dtype_code(w_uk), 0, num_splits)
+        if n == 0:
+            raise MLAError(MLA_ERR_INVALID_ARG, "no workspace size for these sizes")
+        workspace = torch.empty(n, dtype=torch.uint8, device=q_nope.device)
+    p = build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
+                     softmax_scale, out, lse, workspace, num_splits=num_splits, validate=validate)
+    decode_attn(p, stream)
+    return out, lse

@@ -1,0 +1,121 @@
+"""CPU-side checks of the C ABI: the library builds and loads, exports every
+symbol the header declares, and its host logic (argument checks, planner,
+workspace sizing, softmax scale) behaves as documented.  No GPU work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+
+@pytest.fixture(scope="module")
+def mla():
+    from decode_attention_absorbed_amd import build, mla as m
+    if not os.path.exists(m.LIB_PATH):
+        build.build()
+    m.lib()
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("mla_rope_freqs", "mla_softmax_scale", "mla_decode_workspace_size", "mla_decode_attn",
+                 "mla_decode_num_splits", "mla_last_error", "mla_decode_params_size"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(mla):
+    L = ctypes.CDLL(mla.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_params_layout_matches(mla):
+    assert mla.lib().mla_decode_params_size() == ctypes.sizeof(mla.DecodeParams)
+
+
+def test_softmax_scale_host(mla):
+    for rope in (W.ROPE_YARN, W.ROPE_PLAIN):
+        assert mla.softmax_scale(192, rope) == pytest.approx(
+            oracle.softmax_scale(192, oracle.RopeConfig(**rope)), rel=1e-15)
+    assert mla.lib().mla_softmax_scale(0, ctypes.byref(mla.rope_cfg(W.ROPE_YARN))) < 0
+
+
+def test_planner_and_workspace(mla):
+    # one attention workgroup per CU: B * head_groups * splits <= CUs
+    for B in (1, 2, 8, 32, 64, 128, 300):
+        S = mla.num_splits(B, 128, 2048, mla.MLA_DTYPE_BF16, 256)
+        assert S >= 1
+        if B * 2 < 256:
+            assert B * 2 * S <= 256
+        else:
+            assert S == 1
+    assert mla.num_splits(1, 128, 1001, mla.MLA_DTYPE_BF16, 256) == 8   # >= 2 tiles of 64 rows each
+    assert mla.num_splits(4, 16, 65, mla.MLA_DTYPE_F32, 256) == 1
+    a = mla.workspace_size(32, 128, 2048, 1, 1, 256, 0)
+    b = mla.workspace_size(32, 128, 2048, 1, 1, 256, 8)
+    assert 0 < a < b
+    assert mla.workspace_size(0, 128, 2048, 1, 1, 256, 0) == 0
+    assert mla.workspace_size(4, 128, 2048, 7, 1, 256, 0) == 0
+    assert mla.workspace_size(4, 16, 64, 0, 0, 256, 2) == 0          # fp32 path does not split
+
+
+def _params(mla, **kw):
+    p = mla.DecodeParams()
+    p.B, p.H, p.K = 2, 128, 16
+    p.d_nope, p.d_rope, p.d_v, p.kv_rank = 128, 64, 128, 512
+    p.max_cache_len, p.rope_table_len = 64, 64
+    p.dtype_act = p.dtype_w = 1
+    p.dtype_out = 0
+    p.num_cus = 256
+    p.softmax_scale = 0.1
+    fake = 1 << 20                                   # never dereferenced: checks fail first
+    for f in ("q_nope", "q_pe", "w_uk", "w_uv", "kv_cache", "pe_cache", "topk_indices", "cache_lens",
+              "rope_table", "out", "workspace"):
+        setattr(p, f, fake)
+    p.q_nope_stride_b, p.q_nope_stride_h = 128 * 128, 128
+    p.q_pe_stride_b, p.q_pe_stride_h = 128 * 64, 64
+    p.w_uk_stride_h = p.w_uv_stride_h = 128 * 512
+    p.kv_stride_b, p.kv_stride_t = 64 * 512, 512
+    p.pe_stride_b, p.pe_stride_t = 64 * 64, 64
+    p.idx_stride_b = 16
+    p.out_stride_b, p.out_stride_h = 128 * 128, 128
+    p.workspace_size = 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_nope", 64, 2), ("kv_rank", 256, 2), ("dtype_act", 5, 2),
+    ("B", 0, 1), ("K", 0, 1), ("q_nope", 0, 1), ("kv_cache", (1 << 20) + 2, 1),
+    ("kv_stride_t", 513, 1), ("pe_stride_t", 32, 1), ("idx_stride_b", 8, 1),
+    ("softmax_scale", -1.0, 1), ("num_splits", 65, 1), ("flags", 2, 1), ("max_cache_len", 0, 1),
+    ("workspace_size", 0, 3),
+])
+def test_host_checks(mla, field, value, code):
+    p = _params(mla, **{field: value})
+    rc = mla.lib().mla_decode_attn(ctypes.byref(p), None)
+    assert rc == code, mla.last_error()
+    assert mla.last_error()
+
+
+def test_rope_freqs_host_checks(mla):
+    cfg = mla.rope_cfg(dict(W.ROPE_YARN, rope_dim=32))
+    assert mla.lib().mla_rope_freqs(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), None) == mla.MLA_ERR_UNSUPPORTED
+    cfg = mla.rope_cfg(W.ROPE_YARN)
+    assert mla.lib().mla_rope_freqs(ctypes.byref(cfg), None, None) == mla.MLA_ERR_INVALID_ARG
+    cfg = mla.rope_cfg(dict(W.ROPE_YARN, theta=0.5))
+    assert mla.lib().mla_rope_freqs(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), None) == mla.MLA_ERR_INVALID_ARG
