@@ -48,11 +48,10 @@ bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_split
         pl->nhg = 0; pl->heads_per_wg = 1; pl->hgroups = H; pl->splits = 1; pl->tile_rows = 256;
         return forced_splits <= 1;
     }
-    const int need = (H + 31) / 32;
-    pl->nhg = need >= 2 ? 2 : 1;                    // groups of 32 heads per workgroup
-    pl->heads_per_wg = 32 * pl->nhg;
-    pl->hgroups = (H + pl->heads_per_wg - 1) / pl->heads_per_wg;
-    pl->tile_rows = pl->nhg == 4 ? 32 : 64;
+    pl->nhg = 2;                                    // 64 heads per attention workgroup
+    pl->heads_per_wg = 64;
+    pl->hgroups = (H + 63) / 64;
+    pl->tile_rows = 32;
     int S;
     if (forced_splits > 0) {
         S = forced_splits;

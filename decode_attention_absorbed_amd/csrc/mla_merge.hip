@@ -39,20 +39,39 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int dh = k8 & 1, h = (k8 >> 1) * 8 + xcd;
     if (h >= a.H) return;
 
+    // fp32 weights enter as bf16 hi + lo parts (two MFMAs each).
+    constexpr int NP = sizeof(WT) == 4 ? 2 : 1;
     const WT* W = (const WT*)a.w_uv + h * a.wv_sh;
-    bf16x8 bw[2][8];
+    bf16x8 bw[NP][2][8];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int d = 64 * dh + 32 * nb + l32;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-            bw[nb][kb] = load8_bf16<WT>(W + d * RANK + 128 * wave + 16 * kb + 8 * g);
+        for (int kb = 0; kb < 8; ++kb) {
+            const WT* src = W + d * RANK + 128 * wave + 16 * kb + 8 * g;
+            if constexpr (NP == 2) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float wv = to_f32(src[j]);
+                    const bf16 hi = (bf16)wv;
+                    bw[0][nb][kb][j] = hi;
+                    bw[NP - 1][nb][kb][j] = (bf16)(wv - (float)hi);
+                }
+            } else {
+                bw[0][nb][kb] = load8_bf16<WT>(src);
+            }
+        }
     }
 
     for (int b0 = 0; b0 < a.B; b0 += 32) {
         const int bA = b0 + l32;
         f32x16 acc[2] = {f32x16{}, f32x16{}};
         float M = -INFINITY, Wsum = 0.f;
+        // A operand: the merged latent of sequence bA (zero past the batch);
+        // the MFMAs below run with every lane active.
+        bf16x8 av[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) av[kb] = bf16x8{};
         if (bA < a.B) {
             const float* ls = a.lsepart + (long long)bA * a.S * a.H + h;
             for (int s = 0; s < a.S; ++s) M = fmaxf(M, ls[(long long)s * a.H]);
@@ -73,22 +92,17 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
                     for (int j = 0; j < 8; ++j) xs[kb][j] = fmaf(ws, (float)v[j], xs[kb][j]);
                 }
             }
-            bf16x8 av[8];
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) av[kb][j] = f2bf(xs[kb][j]);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) acc[nb] = mfma32(av[kb], bw[nb][kb], acc[nb]);
-        } else {
-            bf16x8 av = bf16x8{};
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb) acc[nb] = mfma32(av, bw[nb][kb], acc[nb]);
         }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
         if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
             a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
         __syncthreads();                        // previous block's reads of red[] done

@@ -163,15 +163,18 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 
 // q_abs for head h, latent columns [256*half, 256*half + 256), every
 // sequence, with bf16 MFMA: M = sequences (32 per block), N = latent
-// columns, K = the 128 content features.  Wave w owns 64 columns.
+// columns, K = the 128 content features.  Wave w owns 64 columns.  fp32
+// weights are split into bf16 hi + lo parts (two MFMAs each), so they enter
+// with ~16 significant bits instead of 8.
 template <typename WT>
 __device__ void absorb_bf16(const PrepArgs& a, int h, int half) {
+    constexpr int NP = sizeof(WT) == 4 ? 2 : 1;       // weight parts
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
     const WT* W = (const WT*)a.w_uk + h * a.wk_sh;
     // B operand: B[k = d][n = c] = W_UK[h][d][c]; lane holds d = 16kb + 8g + j.
-    bf16x8 bw[2][8];
+    bf16x8 bw[NP][2][8];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int c = c0 + 32 * nb + l32;
@@ -180,7 +183,10 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int d = 16 * kb + 8 * g + j;
-                bw[nb][kb][j] = (bf16)to_f32(W[d * RANK + c]);
+                const float wv = to_f32(W[d * RANK + c]);
+                const bf16 hi = (bf16)wv;
+                bw[0][nb][kb][j] = hi;
+                if constexpr (NP == 2) bw[NP - 1][nb][kb][j] = (bf16)(wv - (float)hi);
             }
         }
     }
@@ -199,7 +205,9 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half) {
         for (int nb = 0; nb < 2; ++nb) {
             f32x16 acc = {};
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) acc = mfma32(aq[kb], bw[nb][kb], acc);
+            for (int kb = 0; kb < 8; ++kb)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) acc = mfma32(aq[kb], bw[pp][nb][kb], acc);
             const int c = c0 + 32 * nb + l32;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {

@@ -62,7 +62,7 @@ def test_planner_and_workspace(mla):
             assert B * 2 * S <= 256
         else:
             assert S == 1
-    assert mla.num_splits(1, 128, 1001, mla.MLA_DTYPE_BF16, 256) == 8   # >= 2 tiles of 64 rows each
+    assert mla.num_splits(1, 128, 1001, mla.MLA_DTYPE_BF16, 256) == 16  # >= 2 tiles of 32 rows each
     assert mla.num_splits(4, 16, 65, mla.MLA_DTYPE_F32, 256) == 1
     a = mla.workspace_size(32, 128, 2048, 1, 1, 256, 0)
     b = mla.workspace_size(32, 128, 2048, 1, 1, 256, 8)
