@@ -48,9 +48,9 @@ bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_split
         pl->nhg = 0; pl->heads_per_wg = 1; pl->hgroups = H; pl->splits = 1; pl->tile_rows = 256;
         return forced_splits <= 1;
     }
-    pl->nhg = 2;                                    // 64 heads per attention workgroup
-    pl->heads_per_wg = 64;
-    pl->hgroups = (H + 63) / 64;
+    pl->nhg = 4;                                    // 128 heads per attention workgroup
+    pl->heads_per_wg = 128;
+    pl->hgroups = (H + 127) / 128;
     pl->tile_rows = 32;
     int S;
     if (forced_splits > 0) {
@@ -181,6 +181,10 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream) {
         p->w_uk_stride_h < 128 * 512 || p->w_uv_stride_h < 128 * 512 || p->idx_stride_b < p->K ||
         p->out_stride_h < 128)
         return fail(MLA_ERR_INVALID_ARG, "a stride is smaller than the row it steps over");
+    // the attention kernel addresses one sequence's cache rows with 32-bit byte offsets
+    if ((int64_t)(p->max_cache_len - 1) * p->kv_stride_t * 2 + 1024 > INT32_MAX ||
+        (int64_t)(p->max_cache_len - 1) * p->pe_stride_t * 2 + 128 > INT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "one sequence's cache rows span more than 2 GiB");
 
     int num_cus = p->num_cus;
     if (num_cus == 0 && query_num_cus(&num_cus) != 0) return fail(MLA_ERR_HIP, "cannot query the device");

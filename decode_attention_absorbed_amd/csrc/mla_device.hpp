@@ -55,6 +55,24 @@ __device__ __forceinline__ void global_to_lds16(const void* src, MLA_LDS void* l
     __builtin_amdgcn_global_load_lds(src, lds_base, 16, 0, 0);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Buffer -> LDS copy (buffer_load ... lds): lane l writes its `size` bytes at
+// lds_base + size * l.  lds_base must be wave-uniform.  Unlike the global
+// form, the compiler does not treat the buffer form as a possible LDS access
+// through FLAT, so LDS reads issued while such copies are in flight keep
+// exact lgkmcnt waits.
+__device__ __forceinline__ void buffer_to_lds16(rsrc_t r, uint32_t voff, MLA_LDS void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void buffer_to_lds4(rsrc_t r, uint32_t voff, MLA_LDS void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_base, 4, voff, 0, 0, 0);
+}
+
 // s_waitcnt vmcnt(N): wait until at most N vector memory loads of this wave
 // (global->LDS copies included) are outstanding.  gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima.

@@ -54,18 +54,20 @@ def test_softmax_scale_host(mla):
 
 
 def test_planner_and_workspace(mla):
-    # one attention workgroup per CU: B * head_groups * splits <= CUs
-    for B in (1, 2, 8, 32, 64, 128, 300):
-        S = mla.num_splits(B, 128, 2048, mla.MLA_DTYPE_BF16, 256)
-        assert S >= 1
-        if B * 2 < 256:
-            assert B * 2 * S <= 256
-        else:
-            assert S == 1
+    # one attention workgroup per CU: B * head_groups * splits <= CUs, where
+    # a workgroup takes 128 heads
+    for H, hg in ((128, 1), (16, 1), (256, 2)):
+        for B in (1, 2, 8, 32, 64, 128, 300):
+            S = mla.num_splits(B, H, 2048, mla.MLA_DTYPE_BF16, 256)
+            assert S >= 1
+            if B * hg < 256:
+                assert B * hg * S <= 256 and B * hg * (S + 1) > 256 or S == 32
+            else:
+                assert S == 1
     assert mla.num_splits(1, 128, 1001, mla.MLA_DTYPE_BF16, 256) == 16  # >= 2 tiles of 32 rows each
     assert mla.num_splits(4, 16, 65, mla.MLA_DTYPE_F32, 256) == 1
     a = mla.workspace_size(32, 128, 2048, 1, 1, 256, 0)
-    b = mla.workspace_size(32, 128, 2048, 1, 1, 256, 8)
+    b = mla.workspace_size(32, 128, 2048, 1, 1, 256, 16)
     assert 0 < a < b
     assert mla.workspace_size(0, 128, 2048, 1, 1, 256, 0) == 0
     assert mla.workspace_size(4, 128, 2048, 7, 1, 256, 0) == 0
