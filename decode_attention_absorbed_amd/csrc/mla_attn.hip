@@ -1,27 +1,31 @@
 // Split-KV sparse attention over the latent cache (bf16 MFMA, fp32 accumulation).
 //
 // Computes, for one sequence b, one split s of its selected positions and a
-// group of 32*NHG heads, the partial softmax-weighted latent sum
+// group of 128 heads, the partial softmax-weighted latent sum
 //   o[h, :] = sum_t exp2(x[h,t] - m[h]) C[b,t,:],  l[h] = sum_t exp2(x[h,t] - m[h]),
 //   x[h,t] = scale * log2(e) * (Q~[b,h,:] . [C[b,t,:] ; R[b,t,:]])
 // and writes o / l (bf16) and m + log2(l).  The scores are the latent plus
 // rotary dot products of the MQA decode branch; positions outside the
 // selection never enter (their additive mask is -inf, exp2 gives 0).
 // Source: atlas page "Rotated query part" (also "Query content heads",
-// "Attention weights"), excerpt mla-decode; split-KV partitioning and the
-// online softmax are this library's, not the pages'.
+// "Attention weights"), excerpt mla-decode; the split-KV partition and the
+// softmax bookkeeping are this library's, not the pages'.
 //
-// Workgroup: 4 waves (one per SIMD), 32*NHG heads, tiles of R = 32*RG
-// gathered rows staged in LDS by direct global->LDS copies.
-//   QK^T: wave (hg, rg) computes S^T[32 rows][32 heads] = K_tile . Q^T with
-//         v_mfma_f32_32x32x16_bf16 (M = rows, N = heads, K = 576); its 32
-//         heads of Q~ stay in registers for the whole split.
-//   softmax: per head (one lane column), in-lane max over 16 rows plus one
-//         cross-half shuffle; lazy rescaling (the running max only moves when
-//         a score exceeds it by 2^8).
-//   PV:   wave w owns latent columns [128w, 128w+128) for every head of the
-//         workgroup: O^T[c][h] += V^T[c][t] . P^T[t][h], V^T read with
-//         ds_read_b64_tr_b16, P^T shared through LDS.
+// Workgroup: 4 waves (one per SIMD), 128 heads, tiles of 32 selected rows
+// copied into a 4-stage LDS ring by buffer->LDS DMA, each wave copying 8
+// rows.  Every selected row is read from HBM once per (sequence, split).
+// Wave w owns heads 32w..32w+31 from scores to output:
+//   QK^T: S^T[32 rows][32 heads] = K_tile . Q~^T, v_mfma_f32_32x32x16_bf16
+//         (M = rows, N = heads, K = 576).  The wave's Q~ is held in
+//         registers (33 of 36 feature blocks) and LDS (3 blocks).
+//   softmax: in registers; each lane holds 16 rows of one head.
+//   PV:   O^T[512 columns][32 heads] += V^T . P^T, v_mfma_f32_32x32x16_bf16
+//         (M = columns, N = heads, K = rows).  P^T comes straight from the
+//         QK^T accumulator: the rows of the contraction are ordered to match
+//         the accumulator layout, and V^T is read in that order with
+//         ds_read_b64_tr_b16.  O^T lives in the 256 AGPRs.
+// No wave waits for another's softmax, so QK^T and PV read the same stage
+// and three tiles are in flight while one is consumed.
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
 
@@ -40,41 +44,29 @@ struct AttnArgs {
     float* lsepart;
 };
 
-// ---------------------------------------------------------------------------
-// Workgroup shape: 4 waves (one per SIMD), 128 heads, tiles of 32 gathered
-// rows, a ring of three LDS stages (PV reads tile t, QK reads tile t+1, the
-// copies of tile t+2 are in flight).  Every selected row is gathered once
-// per (sequence, split), and the staged tile feeds all 128 heads.
-// ---------------------------------------------------------------------------
 constexpr int HW = 128;                // heads per workgroup
 constexpr int R = 32;                  // rows per tile
-constexpr int NST = 3;                 // LDS stages
+constexpr int NST = 4;                 // LDS stages
 constexpr int LAT = R * RANK * 2;      // latent region of a stage: row r at r * 1 KB
 constexpr int STAGE = R * ROW * 2;     // + rotary region: row r at LAT + r * 128
-constexpr int PST = R + 8;             // P^T row stride (elements): 80 bytes
-constexpr int PBYTES = HW * PST * 2;
-constexpr int NSLOT = 3;               // index ring slots
-constexpr int OFF_P = NST * STAGE;                 // two P^T buffers
-constexpr int OFF_IDX = OFF_P + 2 * PBYTES;        // [NSLOT][4 waves][8] int: row indices
-constexpr int OFF_L = OFF_IDX + NSLOT * 4 * 8 * 4; // [HW] float
-constexpr int OFF_M = OFF_L + HW * 4;              // [HW] float
-constexpr int OFF_FLAG = OFF_M + HW * 4;
-constexpr int QK_REG = 29;                         // Q~ feature blocks 0..28 live in registers,
-constexpr int QK_LDS = ROW / 16 - QK_REG;          // blocks 29..35 in LDS: [block][head][16]
+constexpr int NSLOT = 4;               // index ring slots
+constexpr int OFF_IDX = NST * STAGE;               // [NSLOT][4 waves][8] int: row indices
+constexpr int OFF_FLAG = OFF_IDX + NSLOT * 4 * 8 * 4;
+constexpr int QK_REG = 33;                         // Q~ feature blocks 0..32 live in registers,
+constexpr int QK_LDS = ROW / 16 - QK_REG;          // blocks 33..35 in LDS: [block][head][16]
 constexpr int OFF_Q = OFF_FLAG + 16;
 constexpr int LDS_BYTES = OFF_Q + QK_LDS * HW * 32;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 // Tile layout in LDS.  Latent region: row r at r * 1024 bytes, its 16-byte
-// chunk c (8 latent features) at slot c ^ swz(r), swz(r) = ((r&3)<<2)|((r>>2)&3).
-// 16 consecutive rows read at one chunk (QK^T operand) hit 16 different bank
-// groups, and the 4 row x 4 chunk blocks of the transposed PV reads do too.
+// chunk c (8 latent features) at slot c ^ swz(r), swz(r) = ((r&3)<<2)|((r>>2)&3),
+// so that both the QK^T operand reads (16 rows at one chunk) and the
+// transposed PV reads (4 rows x 4 chunks per 16 lanes) spread over all banks.
 // Rotary region: row r at r * 128 bytes, chunk c' (0..7) at slot c' ^ ((r>>1)&7).
 __device__ __forceinline__ int lat_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // The wave index, known to the compiler as wave-uniform (an SGPR).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
-
 
 // Largest exponent (log2) a probability may reach relative to the
 // reference maximum before the split is recomputed with the exact maximum.
@@ -83,16 +75,16 @@ constexpr float P_EXP_LIMIT = 64.f;
 // s_waitcnt vmcnt(n) for the counts the copy pipeline produces.
 __device__ __forceinline__ void wait_vm(int n) {
     switch (n) {
-        case 11: wait_vmcnt<11>(); break;
-        case 10: wait_vmcnt<10>(); break;
+        case 20: wait_vmcnt<20>(); break;
+        case 19: wait_vmcnt<19>(); break;
+        case 18: wait_vmcnt<18>(); break;
         case 9: wait_vmcnt<9>(); break;
-        case 1: wait_vmcnt<1>(); break;
         default: wait_vmcnt<0>(); break;
     }
 }
 
 // Workgroup barrier for the main loop.  It waits for this wave's LDS
-// operations only: the global->LDS copies still in flight target stages no
+// operations only: the buffer->LDS copies still in flight target stages no
 // one reads before a later, explicit vmcnt wait (__syncthreads would drain
 // them).  The asm memory clobber keeps the compiler from moving LDS accesses
 // across it.
@@ -100,6 +92,12 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
 }
+
+// Keeps the compiler from hoisting per-read address arithmetic out of the
+// tile loop (which would hold one register per distinct address) or turning
+// lane-dependent loop terms into induction variables that live in VGPRs
+// across the whole kernel.
+__device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
 
 struct SplitCtx {
     int b, s, h0, start, end, ntiles;
@@ -112,20 +110,11 @@ struct SplitCtx {
 // bases leave zero, so every operand address is a base XOR a constant.
 //   QK latent chunk 16j + 2k + lane/32 of row lane%32:  (qk ^ (k << 5)) + 256 j
 //   QK rotary chunk 2k + lane/32:                       rot ^ (k << 5)
-//   PV transposed read rd of rows 16 kt.., block cb:    (tr[rd] ^ (cb << 6)) + 16384 kt
-//   Q~ block 29 + i (LDS part):                         q + 4096 i
+//   PV read rd of column block cb (32 columns), rows 16 kt + 8 rd + 4 (lane/32) + 0..3:
+//                                                       (tr[rd] ^ ((cb & 3) << 6)) + 256 (cb >> 2) + 16384 kt
+//   Q~ block 33 + i (LDS part):                         q + 4096 i
 struct LaneOffsets {
-    int qk, rot, tr[2];
-    int p_wr;           // P^T elements written by this lane (+ 8 j)
-    int p_rd;           // P^T operand read by this lane (+ 32 nb * PST + 16 kt)
-    int q;
-};
-
-// Softmax state of this wave's 32 heads and the O^T accumulators of its
-// 128 latent columns x 128 heads.
-struct PassState {
-    float m_ref, m_true, lsum;
-    f32x16 o[4][4];     // [nb: 32-head block][cb: 32-column block]
+    int qk, rot, tr[2], q;
 };
 
 __device__ __forceinline__ LaneOffsets lane_offsets() {
@@ -137,30 +126,21 @@ __device__ __forceinline__ LaneOffsets lane_offsets() {
     lo.qk = l32 * 1024 + ((g ^ (sw & 1)) << 4) + ((sw >> 1) << 5);
     const int u = (l32 >> 1) & 7;
     lo.rot = LAT + l32 * 128 + ((g ^ (u & 1)) << 4) + ((u >> 1) << 5);
-    // transposed reads: 16-lane block blk reads rows 8 (blk >> 1) + 4 rd + L/4
-    // (+ 16 kt); their swizzle has low bits (2 (blk >> 1) + rd) & 3 and high
-    // bits L/4, the same for both kt
-    const int blk = lane >> 4, L = lane & 15;
-    const int c0 = 2 * (blk & 1) + ((L & 3) >> 1);
-    const int within = (L & 1) * 8;
+    // Transposed reads: in 16-lane block blk, lane 4j + qq addresses row
+    // 8 rd + 4 (blk >> 1) + j, columns 16 (blk & 1) + 4 qq .. +3 of the column
+    // block; lane i of the block receives column 16 (blk & 1) + i of the rows
+    // 8 rd + 4 (blk >> 1) + 0..3.  The row's swizzle has high bits j and low
+    // bits (2 rd + (blk >> 1)) & 3, whatever kt and cb.
+    const int blk = lane >> 4, L = lane & 15, j = L >> 2, qq = L & 3;
 #pragma unroll
     for (int rd = 0; rd < 2; ++rd) {
-        const int r = 8 * (blk >> 1) + 4 * rd + (L >> 2);
-        const int s = lat_swz(r);
-        lo.tr[rd] = r * 1024 + ((16 * wave + (c0 ^ (s & 3))) << 4) + within + ((s >> 2) << 6);
+        const int lowsw = (2 * rd + (blk >> 1)) & 3;
+        lo.tr[rd] = (8 * rd + 4 * (blk >> 1) + j) * 1024 + (((2 * (blk & 1) + (qq >> 1)) ^ lowsw) << 4) +
+                    (qq & 1) * 8 + (j << 6);
     }
-    lo.p_wr = (wave * 32 + l32) * PST + 4 * g;
-    lo.p_rd = l32 * PST + 8 * g;
     lo.q = OFF_Q + (wave * 32 + l32) * 32 + 16 * g;
     return lo;
 }
-
-// Keeps the compiler from hoisting per-read address arithmetic out of the
-// tile loop (which would hold one register per distinct address) or turning
-// lane-dependent loop terms into induction variables that live in VGPRs
-// across the whole kernel.
-__device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
-
 
 // Row indices of tile T for this wave: lanes 0..7 copy 4 bytes each into the
 // ring slot (positions past the end repeat the last row, so every tile costs
@@ -213,7 +193,8 @@ __device__ __forceinline__ void qk_settle(f32x16& acc) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(acc));
 }
 
-// QK^T of one tile for this wave's 32 heads: S^T[32 rows][32 heads]; tile
+// QK^T of one tile for this wave's 32 heads: S^T[32 rows][32 heads] in acc
+// (lane l: head l%32, rows 8(i/4) + 4(l/32) + i%4 for i = 0..15); tile
 // operands are read two steps ahead of the MFMAs.
 __device__ __forceinline__ void qk_tile(const char* __restrict__ st, const char* __restrict__ smem_q,
                                         LaneOffsets lo, const bf16x8 (&qreg)[QK_REG], f32x16& acc) {
@@ -237,94 +218,77 @@ __device__ __forceinline__ void qk_tile(const char* __restrict__ st, const char*
     qk_settle(acc);
 }
 
-// Softmax of 4 consecutive rows (8j + 4g .. +3) of this lane's head:
-// scale, mask rows past the end, exponentiate against the reference maximum.
-__device__ __forceinline__ bf16x4 soft4(PassState& ps, const f32x16& acc, int j, int rem, float scale_log2) {
-    bf16x4 pk;
+// Softmax state of this lane's head (half of its rows: the other half is in
+// lane ^ 32) and the O^T accumulators of the wave's 32 heads.
+struct PassState {
+    float m_ref, m_true, lsum;
+    f32x16 o[16];       // [cb]: columns 32cb + 8(i/4) + 4(lane/32) + i%4 of head lane%32
+};
+
+// Probabilities of accumulator entries 8kt .. 8kt+7 (rows 16kt + 8(e/4) +
+// 4(lane/32) + e%4): scale, mask rows past the end, exponentiate against the
+// reference maximum; returned as the PV B operand of K step kt.
+__device__ __forceinline__ bf16x8 soft8(PassState& ps, const f32x16& acc, int kt, int rem, float scale_log2) {
+    bf16x8 pk;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float x = 8 * j + r < rem ? acc[4 * j + r] * scale_log2 : -INFINITY;
+    for (int e = 0; e < 8; ++e) {
+        const int i = 8 * kt + e;
+        const float x = 8 * (i >> 2) + (i & 3) < rem ? acc[i] * scale_log2 : -INFINITY;
         ps.m_true = fmaxf(ps.m_true, x);
         const float p = __builtin_amdgcn_exp2f(fminf(x - ps.m_ref, P_EXP_LIMIT));
         ps.lsum += p;
-        pk[r] = f2bf(p);
+        pk[e] = f2bf(p);
     }
     return pk;
 }
 
-// PV of one tile (O^T += V^T . P^T) with, when has_next, the softmax of the
-// next tile interleaved (acc in, P^T of the next tile out).
-__device__ __forceinline__ void pv_tile(const char* __restrict__ st, const bf16* __restrict__ p_in,
-                                        bf16* __restrict__ p_out, LaneOffsets lo, PassState& ps,
-                                        const f32x16& acc, bool has_next, int rem_next, float scale_log2) {
+// PV of one tile: O^T[cb] += V^T(kt, cb) . P^T(kt) for 16 column blocks and
+// two K steps of 16 rows.  The K index k = 8 (lane/32) + e of step kt is row
+// 16kt + 8(e/4) + 4(lane/32) + e%4, matching soft8's operand; the A operand
+// (columns x those rows) is two transposed reads of 4 rows each.  The second
+// K step's probabilities are computed while the first step's MFMAs run.
+__device__ __forceinline__ void pv_tile(const char* __restrict__ st, LaneOffsets lo, PassState& ps,
+                                        const f32x16& acc, int rem, float scale_log2) {
     opaque(lo.tr[0]);
     opaque(lo.tr[1]);
-    const bf16* pb = p_in + lo.p_rd;
     auto tr = [&](int kt, int cb) {
-        const bf16x4 lo0 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[0] ^ (cb << 6)) + 16384 * kt));
-        const bf16x4 hi0 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[1] ^ (cb << 6)) + 16384 * kt));
-        return cat(lo0, hi0);
+        const int o = 256 * (cb >> 2) + 16384 * kt;
+        const bf16x4 r0 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[0] ^ ((cb & 3) << 6)) + o));
+        const bf16x4 r1 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[1] ^ ((cb & 3) << 6)) + o));
+        return cat(r0, r1);
     };
-    bf16x8 av[2], pvb[4];
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) pvb[nb] = *(const bf16x8*)(pb + 32 * nb * PST);
+    bf16x8 av[3];
     av[0] = tr(0, 0);
+    av[1] = tr(0, 1);
+    bf16x8 p0 = soft8(ps, acc, 0, rem, scale_log2);
+    bf16x8 p1;
 #pragma unroll
-    for (int step = 0; step < 8; ++step) {
-        const int cb = step & 3;
-        if (step + 1 < 8) av[(step + 1) & 1] = tr((step + 1) >> 2, (step + 1) & 3);
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            ps.o[nb][cb] = mfma32(av[step & 1], pvb[nb], ps.o[nb][cb]);
-            if (step == 3) pvb[nb] = *(const bf16x8*)(pb + 32 * nb * PST + 16);   // P^T rows 16..31
-        }
-        // the softmax of the next tile, one group of 4 rows per step from
-        // step 4 on (the QK^T results are complete by then)
-        if (has_next && step >= 4) {
-            const int j = step - 4;
-            *(bf16x4*)(p_out + lo.p_wr + 8 * j) = soft4(ps, acc, j, rem_next, scale_log2);
-        }
+    for (int step = 0; step < 32; ++step) {
+        const int kt = step >> 4, cb = step & 15;
+        if (step + 2 < 32) av[(step + 2) % 3] = tr((step + 2) >> 4, (step + 2) & 15);
+        ps.o[cb] = mfma32(av[step % 3], kt == 0 ? p0 : p1, ps.o[cb]);
+        if (step == 3) p1 = soft8(ps, acc, 1, rem, scale_log2);
         __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-// One main-loop iteration's work after the barrier: copy tile it+2 and the
-// indices of tile it+4, QK^T of tile it+1, PV of tile it with the softmax
-// of tile it+1.  Distinct restrict-qualified pointers tell the compiler
-// that the reads never touch the stage or slot being filled, so it does not
-// wait for the copies in flight.
-__device__ __forceinline__ void main_step(const AttnArgs& a, const SplitCtx& sc, int it, const LaneOffsets& lo,
-                                          const char* __restrict__ smem_q, const bf16x8 (&qreg)[QK_REG], PassState& ps,
-                                          char* __restrict__ dma_stage, const int* __restrict__ dma_slot,
-                                          int* __restrict__ idx_slot, const char* __restrict__ qk_stage,
-                                          const char* __restrict__ pv_stage, const bf16* __restrict__ p_in,
-                                          bf16* __restrict__ p_out) {
-    const int lane = threadIdx.x & 63;
-    const int g = lane >> 5;
-    const int nt = sc.ntiles;
-    if (it + 2 < nt) issue_tile(a, sc, dma_stage, dma_slot);
-    if (it + 4 < nt) fetch_idx(sc, it + 4, idx_slot);
-    const bool has_next = it + 1 < nt;
-    f32x16 acc;
-    if (has_next) qk_tile(qk_stage, smem_q, lo, qreg, acc);
-    int g4 = 4 * g;
-    opaque(g4);
-    const int rem_next = sc.end - sc.start - (it + 1) * R - g4;
-    pv_tile(pv_stage, p_in, p_out, lo, ps, acc, has_next, rem_next, a.scale_log2);
 }
 
 // One pass over the split (see attn_kernel).  Returns true when the pass
 // must be repeated with the exact maximum (then m_ref holds it).
 //
-// Copy pipeline, per wave and tile T: 9 global->LDS copies issued in
-// iteration T-2 and the 4-byte index copy issued in iteration T-4.
-// Iteration t waits until tile t+1 has landed; only the index copy issued
-// after it may still be in flight.
+// Copy pipeline, per wave: iteration j fetches the indices of tile j+6 and
+// copies tile j+3 (9 copies) into the stage tile j-1 left; the prologue
+// plays iterations -3..-1.  Iteration it waits until tile it has landed:
+// the copies issued after it (indices of it+4 and it+5, tiles it+1 and
+// it+2) may still be in flight.
 __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc, char* smem,
                                           float& m_ref, bool known) {
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int g = lane >> 5, l32 = lane & 31;
+    const int nt = sc.ntiles;
+    int* flag = (int*)(smem + OFF_FLAG);
     __syncthreads();                               // previous pass done
+    if (tid == 0) *flag = 0;
+
     // This wave's 32 heads of Q~ (QK^T B operand): feature block ks (16
     // features) holds features 16 ks + 8 (lane/32) .. +7 of head 32 wave +
     // lane%32; blocks below QK_REG stay in registers, the rest go to LDS.
@@ -341,10 +305,8 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             *(bf16x8*)(qd + 4096 * i) = ok ? *(const bf16x8*)(q + 16 * (QK_REG + i)) : bf16x8{};
     }
 
-    const int start = sc.start, end = sc.end, nt = sc.ntiles;
     int* idx_ring = (int*)(smem + OFF_IDX) + wave * 8;      // + slot * 32
     auto stage = [&](int T) { return smem + (T % NST) * STAGE; };
-    auto pbuf = [&](int T) { return (bf16*)(smem + OFF_P + (T & 1) * PBYTES); };
     auto slot = [&](int T) { return idx_ring + (T % NSLOT) * 32; };
 
     const LaneOffsets lo = lane_offsets();
@@ -353,109 +315,85 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     ps.m_true = known ? m_ref : -INFINITY;
     ps.lsum = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) ps.o[nb][cb] = f32x16{};
+    for (int cb = 0; cb < 16; ++cb) ps.o[cb] = f32x16{};
 
-    // ---- prologue: indices for tiles 0..3, copies for tiles 0 and 1 ----
+    // ---- prologue: indices of tiles 0..5, copies of tiles 0..2 ----
     if (nt > 0) {
-        fetch_idx(sc, 0, slot(0));
-        if (nt > 1) fetch_idx(sc, 1, slot(1));
+#pragma unroll
+        for (int T = 0; T < 3; ++T)
+            if (T < nt) fetch_idx(sc, T, slot(T));
         wait_vmcnt<0>();
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
+        for (int T = 0; T < 3; ++T) {
+            if (T + 3 < nt) fetch_idx(sc, T + 3, slot(T + 3));
             if (T < nt) issue_tile(a, sc, stage(T), slot(T));
-            if (T + 2 < nt) fetch_idx(sc, T + 2, slot(T + 2));
         }
-        wait_vm((nt > 2) + 9 * (nt > 1) + (nt > 3));
-        __syncthreads();                           // tile 0 visible
-        f32x16 acc;
-        qk_tile(stage(0), smem, lo, qreg, acc);
-        // reference maximum: the first tile's, floored to an integer so that
-        // exp2(x - m_ref) differs from exp2(x) by a power of two only and its
-        // bf16 rounding does not depend on where the splits fall
-        const int rem = end - (start + 4 * g);
-        if (!known) {
-            float mt = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int row = 8 * (i >> 2) + (i & 3);
-                mt = fmaxf(mt, row < rem ? acc[i] * a.scale_log2 : -INFINITY);
-            }
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            ps.m_ref = floorf(mt);
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) *(bf16x4*)(pbuf(0) + lo.p_wr + 8 * j) = soft4(ps, acc, j, rem, a.scale_log2);
     }
 
     // ---- main loop ----
     for (int it = 0; it < nt; ++it) {
-        wait_vm(it + 3 < nt ? 1 : 0);
-        lds_barrier();          // tile it+1 resident, P(it) visible, stage (it-1)%3 free
-        main_step(a, sc, it, lo, smem, qreg, ps, stage(it + 2), slot(it + 2), slot(it + 4), stage(it + 1), stage(it),
-                  pbuf(it), pbuf(it + 1));
+        wait_vm((it + 4 < nt) + 9 * (it + 1 < nt) + (it + 5 < nt) + 9 * (it + 2 < nt));
+        lds_barrier();          // tile it resident and visible; stage (it-1)%4 free
+        if (it + 6 < nt) fetch_idx(sc, it + 6, slot(it + 6));
+        if (it + 3 < nt) issue_tile(a, sc, stage(it + 3), slot(it + 3));
+        f32x16 acc;
+        qk_tile(stage(it), smem, lo, qreg, acc);
+        int g4 = 4 * g;
+        opaque(g4);
+        const int rem = sc.end - sc.start - it * R - g4;
+        if (it == 0 && !known) {
+            // reference maximum: the first tile's, floored to an integer so
+            // that exp2(x - m_ref) differs from exp2(x) by a power of two only
+            // and its bf16 rounding does not depend on where the splits fall
+            float mt = -INFINITY;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                mt = fmaxf(mt, 8 * (i >> 2) + (i & 3) < rem ? acc[i] * a.scale_log2 : -INFINITY);
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            ps.m_ref = floorf(mt);
+        }
+        pv_tile(stage(it), lo, ps, acc, rem, a.scale_log2);
     }
 
     // ---- overflow check, then normalise and write ----
-    float* lred = (float*)(smem + OFF_L);
-    float* mfin = (float*)(smem + OFF_M);
-    int* flag = (int*)(smem + OFF_FLAG);
     __syncthreads();
-    if (tid == 0) *flag = 0;
-    __syncthreads();
-    if (!known && ps.m_true > ps.m_ref + P_EXP_LIMIT) *flag = 1;
-    const float lt = ps.lsum + __shfl_xor(ps.lsum, 32);
     const float mx = fmaxf(ps.m_true, __shfl_xor(ps.m_true, 32));
-    if (g == 0) {
-        lred[wave * 32 + l32] = lt;
-        mfin[wave * 32 + l32] = ps.m_ref;
-    }
+    if (!known && mx > ps.m_ref + P_EXP_LIMIT) *flag = 1;
     __syncthreads();
     if (!known && *flag) {
         m_ref = floorf(mx);
         return true;
     }
-    const long long pbase = ((long long)sc.b * a.S + sc.s) * a.H;
+    const float l = ps.lsum + __shfl_xor(ps.lsum, 32);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int h = sc.h0 + wave * 32 + l32;
+    if (h < a.H) {
+        const long long prow = ((long long)sc.b * a.S + sc.s) * a.H + h;
+        bf16* dst = a.opart + prow * RANK + 4 * g;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        const int hl = nb * 32 + l32, h = sc.h0 + hl;
-        const float l = lred[hl];
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        if (h < a.H) {
-            bf16* dst = a.opart + (pbase + h) * RANK + 128 * wave;
+        for (int cb = 0; cb < 16; ++cb) {
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
+            for (int q4 = 0; q4 < 4; ++q4) {
+                bf16x4 v;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bf16x4 v;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = f2bf(ps.o[nb][cb][4 * j + r] * inv);
-                    *(bf16x4*)(dst + 32 * cb + 8 * j + 4 * g) = v;
-                }
+                for (int r = 0; r < 4; ++r) v[r] = f2bf(ps.o[cb][4 * q4 + r] * inv);
+                *(bf16x4*)(dst + 32 * cb + 8 * q4) = v;
             }
-            if (wave == 0 && g == 0) a.lsepart[pbase + h] = l > 0.f ? mfin[hl] + log2f(l) : -INFINITY;
         }
+        if (g == 0) a.lsepart[prow] = l > 0.f ? ps.m_ref + log2f(l) : -INFINITY;
     }
     return false;
 }
 
-// Split-KV attention workgroup: 4 waves, 128 heads, 32-row tiles.  Wave w:
-// QK role: S^T[32 rows][heads 32w..32w+31] of each tile with
-// v_mfma_f32_32x32x16_bf16 (M = rows, N = heads, K = 576), its heads of Q~
-// held in registers.  PV role: O^T[latent columns 128w..128w+127][128 heads]
-// with v_mfma_f32_32x32x16_bf16 (M = columns, N = heads, K = rows), V^T read
-// with ds_read_b64_tr_b16 and P^T from LDS.  The reference maximum of each
-// head is the (floored) maximum of the split's first tile; later
-// probabilities are exp2(x - m_ref) and may exceed 1 (fp32 and bf16 share
-// the 8-bit exponent), so the accumulators are never rescaled.  If a head's
-// true maximum exceeds m_ref by more than P_EXP_LIMIT the split is run again
-// with the exact maximum as reference.
+// Split-KV attention workgroup (see the top of this file).  The reference
+// maximum of each head is the (floored) maximum of the split's first tile;
+// later probabilities are exp2(x - m_ref) and may exceed 1 (fp32 and bf16
+// share the 8-bit exponent), so the accumulators are never rescaled.  If a
+// head's true maximum exceeds m_ref by more than P_EXP_LIMIT the split is
+// run again with the exact maximum as reference.
 __global__ __attribute__((amdgpu_flat_work_group_size(256, 256), amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) char smem[LDS_BYTES];
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
-    const int g = lane >> 5, l32 = lane & 31;
 
     // XCD-aware mapping: workgroups of the same (sequence, split) and
     // different head groups get ids 8 apart, i.e. the same XCD and L2.
