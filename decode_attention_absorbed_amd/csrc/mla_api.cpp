@@ -169,12 +169,12 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream) {
         if (!aligned16(ptrs[i])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
     }
     if (p->lse_out && ((uintptr_t)p->lse_out & 3u)) return fail(MLA_ERR_INVALID_ARG, "lse_out misaligned");
-    const int64_t vec_strides[] = {p->q_nope_stride_b, p->q_nope_stride_h, p->w_uv_stride_h,
-                                   p->kv_stride_b, p->kv_stride_t, p->pe_stride_b, p->pe_stride_t};
+    const int64_t vec_strides[] = {p->q_nope_stride_b, p->q_nope_stride_h, p->q_pe_stride_b, p->q_pe_stride_h,
+                                   p->w_uk_stride_h, p->w_uv_stride_h, p->kv_stride_b, p->kv_stride_t,
+                                   p->pe_stride_b, p->pe_stride_t};
     for (int64_t st : vec_strides)
-        if (st < 0 || (st & 7)) return fail(MLA_ERR_INVALID_ARG, "q_nope/w_uv/cache strides must be non-negative multiples of 8");
-    const int64_t other[] = {p->q_pe_stride_b, p->q_pe_stride_h, p->w_uk_stride_h, p->idx_stride_b,
-                             p->out_stride_b, p->out_stride_h};
+        if (st < 0 || (st & 7)) return fail(MLA_ERR_INVALID_ARG, "q/weight/cache strides must be non-negative multiples of 8");
+    const int64_t other[] = {p->idx_stride_b, p->out_stride_b, p->out_stride_h};
     for (int64_t st : other)
         if (st < 0) return fail(MLA_ERR_INVALID_ARG, "negative stride");
     if (p->kv_stride_t < 512 || p->pe_stride_t < 64 || p->q_nope_stride_h < 128 || p->q_pe_stride_h < 64 ||

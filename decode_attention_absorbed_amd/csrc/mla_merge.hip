@@ -15,9 +15,10 @@ namespace mla {
 // ---------------------------------------------------------------------------
 // bf16 path: out[b, h, :] = W_UV[h] . sum_s w_{b,s} o_s[b, h, :]
 //   w_{b,s} = 2^(lse_s - M) / sum_s' 2^(lse_s' - M),  M = max_s lse_s.
-// Workgroup (head h, output half dh) covers every sequence.  bf16 MFMA with
-// M = sequences (32 per block), N = 64 outputs, K = 512 latent columns split
-// over the 4 waves (128 each) and reduced through LDS.
+// Workgroup (head h, output half dh) covers every sequence with 8 waves (two
+// per SIMD, so that one wave's loads overlap the other's work).  bf16 MFMA
+// with M = sequences (32 per step), N = 64 outputs, K = 512 latent columns
+// split over the 8 waves (64 each) and reduced through LDS.
 // ---------------------------------------------------------------------------
 struct MergeArgs {
     int B, H, S;
@@ -28,9 +29,12 @@ struct MergeArgs {
     float* lse_out;
 };
 
+constexpr int MW = 8;            // waves per merge workgroup
+constexpr int MKB = RANK / (16 * MW);   // K steps (16 latent columns) per wave
+
 template <typename WT, typename OutT>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
-    __shared__ float red[4 * 2 * 16 * 64];
+__global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
+    __shared__ float red[MW * 2 * 16 * 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     // the two output halves of one head sit 8 ids apart (same XCD, shared L2)
@@ -38,21 +42,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     const int xcd = id & 7, k8 = id >> 3;
     const int dh = k8 & 1, h = (k8 >> 1) * 8 + xcd;
     if (h >= a.H) return;
+    const int col0 = (RANK / MW) * wave;
 
     // fp32 weights enter as bf16 hi + lo parts (two MFMAs each).
     constexpr int NP = sizeof(WT) == 4 ? 2 : 1;
     const WT* W = (const WT*)a.w_uv + h * a.wv_sh;
-    bf16x8 bw[NP][2][8];
+    bf16x8 bw[NP][2][MKB];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
         const int d = 64 * dh + 32 * nb + l32;
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            const WT* src = W + d * RANK + 128 * wave + 16 * kb + 8 * g;
+        for (int kb = 0; kb < MKB; ++kb) {
+            const WT* src = W + d * RANK + col0 + 16 * kb + 8 * g;
             if constexpr (NP == 2) {
+                const f32x4 x0 = *(const f32x4*)src, x1 = *(const f32x4*)(src + 4);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const float wv = to_f32(src[j]);
+                    const float wv = j < 4 ? x0[j] : x1[j - 4];
                     const bf16 hi = (bf16)wv;
                     bw[0][nb][kb][j] = hi;
                     bw[NP - 1][nb][kb][j] = (bf16)(wv - (float)hi);
@@ -67,60 +73,74 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         const int bA = b0 + l32;
         f32x16 acc[2] = {f32x16{}, f32x16{}};
         float M = -INFINITY, Wsum = 0.f;
-        // A operand: the merged latent of sequence bA (zero past the batch);
-        // the MFMAs below run with every lane active.
-        bf16x8 av[8];
+        // A operand: the merged latent of sequence bA over this wave's 64
+        // columns (zero past the batch); splits are taken four at a time so
+        // that their loads are in flight together.  The MFMAs below run with
+        // every lane active.
+        bf16x8 av[MKB];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) av[kb] = bf16x8{};
+        for (int kb = 0; kb < MKB; ++kb) av[kb] = bf16x8{};
         if (bA < a.B) {
             const float* ls = a.lsepart + (long long)bA * a.S * a.H + h;
             for (int s = 0; s < a.S; ++s) M = fmaxf(M, ls[(long long)s * a.H]);
-            for (int s = 0; s < a.S; ++s) Wsum += exp2f(ls[(long long)s * a.H] - M);
-            const float invW = 1.f / Wsum;
-            float xs[8][8];
+            float xs[MKB][8];
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+            for (int kb = 0; kb < MKB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
-            for (int s = 0; s < a.S; ++s) {
-                const float ws = exp2f(ls[(long long)s * a.H] - M) * invW;
-                const bf16* src = a.opart + (((long long)bA * a.S + s) * a.H + h) * RANK + 128 * wave + 8 * g;
+            const bf16* src0 = a.opart + ((long long)bA * a.S * a.H + h) * RANK + col0 + 8 * g;
+            for (int s0 = 0; s0 < a.S; s0 += 4) {
+                bf16x8 v[4][MKB];
+                float ws[4];
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) {
-                    const bf16x8 v = *(const bf16x8*)(src + 16 * kb);
+                for (int u = 0; u < 4; ++u) {
+                    const int s = s0 + u;
+                    ws[u] = s < a.S ? exp2f(ls[(long long)s * a.H] - M) : 0.f;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) xs[kb][j] = fmaf(ws, (float)v[j], xs[kb][j]);
+                    for (int kb = 0; kb < MKB; ++kb)
+                        v[u][kb] = s < a.S ? *(const bf16x8*)(src0 + (long long)s * a.H * RANK + 16 * kb) : bf16x8{};
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    Wsum += ws[u];
+#pragma unroll
+                    for (int kb = 0; kb < MKB; ++kb)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) xs[kb][j] = fmaf(ws[u], (float)v[u][kb][j], xs[kb][j]);
                 }
             }
+            const float invW = 1.f / Wsum;
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+            for (int kb = 0; kb < MKB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) av[kb][j] = f2bf(xs[kb][j]);
+                for (int j = 0; j < 8; ++j) av[kb][j] = f2bf(xs[kb][j] * invW);
         }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+            for (int kb = 0; kb < MKB; ++kb)
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
         if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
             a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
-        __syncthreads();                        // previous block's reads of red[] done
+        __syncthreads();                        // previous step's reads of red[] done
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int i = 0; i < 16; ++i) red[((wave * 2 + nb) * 16 + i) * 64 + lane] = acc[nb][i];
         __syncthreads();
+        // 32 sequences x 64 outputs; D element (row 8(i/4) + 4gg + i%4, column
+        // 32 nb + n) sits at red[w][nb][i][32 gg + n]
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = tid + 256 * k;
+        for (int k = 0; k < 2048 / (64 * MW); ++k) {
+            const int e = tid + 64 * MW * k;
             const int dl = e & 63, bl = e >> 6;
             const int nb = dl >> 5, n = dl & 31;
             const int i = 4 * (bl >> 3) + (bl & 3), gg = (bl >> 2) & 1;
             const int ln = gg * 32 + n;
             float v = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + ln];
+            for (int w = 0; w < MW; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + ln];
             const int bo = b0 + bl;
             if (bo < a.B)
                 ((OutT*)a.out)[bo * a.out_sb + h * a.out_sh + 64 * dh + dl] = from_f32<OutT>(v);
@@ -238,7 +258,7 @@ hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Wo
     a.lse_out = p.lse_out;
     const bool wf = p.dtype_w == MLA_DTYPE_F32, of = p.dtype_out == MLA_DTYPE_F32;
     if (plan.bf16_path) {
-        const dim3 grid(((p.H + 7) / 8) * 16), block(256);
+        const dim3 grid(((p.H + 7) / 8) * 16), block(64 * MW);
         if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), grid, block, 0, s, a);
         else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), grid, block, 0, s, a);
         else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), grid, block, 0, s, a);

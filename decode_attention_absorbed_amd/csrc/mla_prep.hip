@@ -100,7 +100,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_wave) {
 
 // Selection compaction for sequence b: every position listed in the index
 // row (minus -1 slots and entries outside [0, L_b)), once, ascending.
-// Dynamic LDS holds a bitmap of ceil(L_max / 32) words.
+// LDS holds a bitmap of ceil(L_max / 32) words.
 template <typename QtT, typename ActT>
 __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     __shared__ int lds_wave[4];
@@ -115,15 +115,26 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     for (int w = tid; w < nwords; w += 256) bm[w] = 0u;
     __syncthreads();
     const int32_t* row = a.idx + (long long)b * a.idx_sb;
-    for (int j = tid; j < a.K; j += 256) {
-        const int v = row[j];
-        if (v == -1) continue;
-        if (v < 0 || v >= L) { status |= BAD_INDEX_RANGE; continue; }
-        if (v >= Lc) continue;                        // cache length already flagged
+    auto mark = [&](int v) {
+        if (v == -1) return;
+        if (v < 0 || v >= L) { status |= BAD_INDEX_RANGE; return; }
+        if (v >= Lc) return;                          // cache length already flagged
         const uint32_t bit = 1u << (v & 31);
-        const uint32_t old = atomicOr(&bm[v >> 5], bit);
-        if (old & bit) status |= BAD_DUPLICATE;
+        if (a.validate) {
+            const uint32_t old = atomicOr(&bm[v >> 5], bit);
+            if (old & bit) status |= BAD_DUPLICATE;
+        } else {
+            __hip_atomic_fetch_or(&bm[v >> 5], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    };
+    // four indices per thread and step when the row is 16-byte aligned
+    const bool vec = ((uintptr_t)row & 15) == 0;
+    const int kv = vec ? (a.K & ~3) : 0;
+    for (int j = 4 * tid; j < kv; j += 1024) {
+        const int4 v = *(const int4*)(row + j);
+        mark(v.x); mark(v.y); mark(v.z); mark(v.w);
     }
+    for (int j = kv + tid; j < a.K; j += 256) mark(row[j]);
     __syncthreads();
     const int wpt = (nwords + 255) / 256;
     const int w0 = min(tid * wpt, nwords), w1 = min(w0 + wpt, nwords);
@@ -145,16 +156,49 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
         if (total == 0) status |= BAD_EMPTY;
     }
     // Rotary query at p_b = L_b - 1: pairs (2i, 2i+1) are one complex number.
+    // Thread t rotates head t/2, features 32 (t%2) .. +31 (16 pairs).
     const int p = min(max(L - 1, 0), a.Trope - 1);
     const float* cs = a.rope_table + (long long)p * D_ROPE;
-    for (int e = tid; e < a.H * (D_ROPE / 2); e += 256) {
-        const int h = e >> 5, i = e & 31;
-        const ActT* q = (const ActT*)a.q_pe + b * a.qp_sb + h * a.qp_sh;
-        const float x0 = to_f32(q[2 * i]), x1 = to_f32(q[2 * i + 1]);
-        const float c = cs[2 * i], s = cs[2 * i + 1];
-        QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK;
-        dst[2 * i] = from_f32<QtT>(x0 * c - x1 * s);
-        dst[2 * i + 1] = from_f32<QtT>(x0 * s + x1 * c);
+    for (int e = tid; e < a.H * 2; e += 256) {
+        const int h = e >> 1, f0 = 32 * (e & 1);
+        const ActT* q = (const ActT*)a.q_pe + b * a.qp_sb + h * a.qp_sh + f0;
+        float x[32], t[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (sizeof(ActT) == 2) {
+                const bf16x8 v = *(const bf16x8*)(q + 8 * k);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[8 * k + j] = (float)v[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[8 * k + j] = to_f32(q[8 * k + j]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const f32x4 v = *(const f32x4*)(cs + f0 + 4 * k);
+            t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
+        }
+        QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f0;
+        QtT y[32];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float c = t[2 * i], sn = t[2 * i + 1];
+            y[2 * i] = from_f32<QtT>(x[2 * i] * c - x[2 * i + 1] * sn);
+            y[2 * i + 1] = from_f32<QtT>(x[2 * i] * sn + x[2 * i + 1] * c);
+        }
+        if constexpr (sizeof(QtT) == 2) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bf16x8 v;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = y[8 * k + j];
+                *(bf16x8*)(dst + 8 * k) = v;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) dst[i] = y[i];
+        }
     }
     if (status) atomicOr(&lds_status, status);
     __syncthreads();
@@ -162,37 +206,79 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 }
 
 // q_abs for head h, latent columns [256*half, 256*half + 256), every
-// sequence, with bf16 MFMA: M = sequences (32 per block), N = latent
-// columns, K = the 128 content features.  Wave w owns 64 columns.  fp32
-// weights are split into bf16 hi + lo parts (two MFMAs each), so they enter
-// with ~16 significant bits instead of 8.
+// sequence, with bf16 MFMA: M = latent columns, N = sequences (32 per
+// step), K = the 128 content features.  Wave w owns 64 columns.  Its
+// weight slice W_UK[h][0:128][64 columns] is read once with 16-byte loads,
+// converted to bf16 (fp32 weights split into a bf16 high part and a bf16
+// remainder, two MFMAs each, so they enter with ~16 significant bits) and
+// stored row-major in a wave-private LDS region; the MFMA operand (8
+// consecutive features of one column) is then read with ds_read_b64_tr_b16.
+constexpr int ABS_WAVE_LDS = 2 * D_NOPE * 64 * 2;     // two parts x [128][64] bf16
+
 template <typename WT>
-__device__ void absorb_bf16(const PrepArgs& a, int h, int half) {
+__device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
     constexpr int NP = sizeof(WT) == 4 ? 2 : 1;       // weight parts
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
-    const WT* W = (const WT*)a.w_uk + h * a.wk_sh;
-    // B operand: B[k = d][n = c] = W_UK[h][d][c]; lane holds d = 16kb + 8g + j.
-    bf16x8 bw[NP][2][8];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const int c = c0 + 32 * nb + l32;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int d = 16 * kb + 8 * g + j;
-                const float wv = to_f32(W[d * RANK + c]);
-                const bf16 hi = (bf16)wv;
-                bw[0][nb][kb][j] = hi;
-                if constexpr (NP == 2) bw[NP - 1][nb][kb][j] = (bf16)(wv - (float)hi);
+    const WT* W = (const WT*)a.w_uk + h * a.wk_sh + c0;
+    char* wl = lds + wave * ABS_WAVE_LDS;             // part pp, row d, column c at pp*16384 + d*128 + c*2 (swizzled)
+    // Row d holds 64 columns = 8 chunks of 16 bytes; chunk q sits at slot
+    // q ^ (d & 7) so that the transposed reads (4 rows x 16 columns per 16
+    // lanes) do not collide.
+    auto waddr = [&](int pp, int d, int c) {
+        return pp * (D_NOPE * 128) + d * 128 + ((((c >> 3) ^ (d & 7))) << 4) + (c & 7) * 2;
+    };
+    // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i.
+    {
+        const int cq = 4 * (lane & 15);
+#pragma unroll 8
+        for (int i = 0; i < D_NOPE / 4; ++i) {
+            const int d = (lane >> 4) + 4 * i;
+            float v[4];
+            if constexpr (sizeof(WT) == 4) {
+                const f32x4 x = *(const f32x4*)(W + d * RANK + cq);
+                v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
+            } else {
+                const bf16x4 x = *(const bf16x4*)(W + d * RANK + cq);
+                v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
             }
+            bf16x4 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                hi[e] = (bf16)v[e];
+                lo[e] = (bf16)(v[e] - (float)hi[e]);
+            }
+            *(bf16x4*)(wl + waddr(0, d, cq)) = hi;
+            if constexpr (NP == 2) *(bf16x4*)(wl + waddr(1, d, cq)) = lo;
         }
     }
-    for (int b0 = 0; b0 < a.B; b0 += 32) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // this wave's LDS writes done (only it reads them)
+    // Weight operand (A) of K step kb, column block nb: lane l holds column
+    // 32 nb + l%32, features 16 kb + 8 (l/32) .. +7 -- two transposed reads of
+    // 4 rows each.  In a 16-lane block, lane 4j + q addresses row
+    // 16 kb + 8 (blk >> 1) + 4 rr + j, columns 32 nb + 16 (blk & 1) + 4 q .. +3.
+    const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
+    auto bop = [&](int pp, int nb, int kb) {
+        bf16x4 r[2];
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            const int d = 16 * kb + 8 * (blk >> 1) + 4 * rr + jj;
+            const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
+            r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(pp, d, c)));
+        }
+        return cat(r[0], r[1]);
+    };
+    bf16x8 bw[NP][2][8];
+#pragma unroll
+    for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) bw[pp][nb][kb] = bop(pp, nb, kb);
+
+    auto load_q = [&](int b0, bf16x8 (&aq)[8]) {
         const int bA = b0 + l32;
-        bf16x8 aq[8];
         if (bA < a.B) {
             const bf16* q = (const bf16*)a.q_nope + bA * a.qn_sb + h * a.qn_sh;
 #pragma unroll
@@ -201,18 +287,34 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half) {
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) aq[kb] = bf16x8{};
         }
+    };
+    bf16x8 aqn[8];
+    load_q(0, aqn);
+    for (int b0 = 0; b0 < a.B; b0 += 32) {
+        const int bA = b0 + l32;
+        bf16x8 aq[8];
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) aq[kb] = aqn[kb];
+        if (b0 + 32 < a.B) load_q(b0 + 32, aqn);     // next sequences' queries in flight
+        // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
+        // sequence b0 + l%32 and columns 8(i/4) + 4(l/32) + i%4, so each lane
+        // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             f32x16 acc = {};
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int pp = 0; pp < NP; ++pp) acc = mfma32(aq[kb], bw[pp][nb][kb], acc);
-            const int c = c0 + 32 * nb + l32;
+                for (int pp = 0; pp < NP; ++pp) acc = mfma32(bw[pp][nb][kb], aq[kb], acc);
+            if (bA < a.B) {
+                bf16* dst = (bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 32 * nb + 4 * g;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int bo = b0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (bo < a.B) ((bf16*)a.qt)[((long long)bo * a.H + h) * ROW + c] = f2bf(acc[i]);
+                for (int i4 = 0; i4 < 4; ++i4) {
+                    bf16x4 v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) v[r] = f2bf(acc[4 * i4 + r]);
+                    *(bf16x4*)(dst + 8 * i4) = v;
+                }
             }
         }
     }
@@ -235,16 +337,26 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
     }
 }
 
+// Block bid computes absorption slice bid (head bid/2, half bid%2) when
+// bid < 2H, then the selection and rotary query of sequences bid,
+// bid + gridDim.x, ...  The dynamic LDS serves both parts in turn.
+// LDS of a prep block: the absorption's weight staging (4 waves) and, in
+// turn, the selection bitmap of up to 2^20 positions.
+constexpr int PREP_LDS = 4 * ABS_WAVE_LDS;
+static_assert(PREP_LDS >= (1 << 20) / 8, "bitmap of the largest cache");
+
 template <typename ActT, typename WT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    extern __shared__ uint32_t dyn_lds[];
+    __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[PREP_LDS / 4];
     const int bid = blockIdx.x;
     if (bid < a.n_absorb) {
         const int h = bid >> 1, half = bid & 1;
-        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half);
+        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half, (char*)dyn_lds);
         else absorb_f32<WT>(a, h, half);
-    } else {
-        prep_sequence<ActT, ActT>(a, bid - a.n_absorb, dyn_lds);
+    }
+    for (int b = bid; b < a.B; b += gridDim.x) {
+        __syncthreads();                              // LDS free for the bitmap
+        prep_sequence<ActT, ActT>(a, b, dyn_lds);
     }
 }
 
@@ -259,23 +371,14 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     a.idx = p.topk_indices; a.idx_sb = p.idx_stride_b;
     a.cache_lens = p.cache_lens; a.rope_table = p.rope_table;
     a.qt = w.qt; a.list = w.list; a.counts = w.counts; a.status = w.status;
-    const size_t lds = (size_t)((p.max_cache_len + 31) / 32) * 4;
-    const dim3 grid(a.n_absorb + p.B), block(256);
+    const dim3 grid(a.n_absorb > p.B ? a.n_absorb : p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;
-    if (lds > 48 * 1024) {
-        const void* fns[] = {(const void*)prep_kernel<bf16, float>, (const void*)prep_kernel<bf16, bf16>,
-                             (const void*)prep_kernel<float, float>, (const void*)prep_kernel<float, bf16>};
-        for (const void* f : fns) {
-            hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-            if (e != hipSuccess) return e;
-        }
-    }
     if (plan.bf16_path) {
-        if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float>), grid, block, lds, s, a);
-        else hipLaunchKernelGGL((prep_kernel<bf16, bf16>), grid, block, lds, s, a);
+        if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<bf16, bf16>), grid, block, 0, s, a);
     } else {
-        if (wf) hipLaunchKernelGGL((prep_kernel<float, float>), grid, block, lds, s, a);
-        else hipLaunchKernelGGL((prep_kernel<float, bf16>), grid, block, lds, s, a);
+        if (wf) hipLaunchKernelGGL((prep_kernel<float, float>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<float, bf16>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }

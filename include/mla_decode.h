@@ -129,12 +129,13 @@ typedef struct mla_decode_params {
     uint32_t flags;            /* MLA_FLAG_* */
     float   softmax_scale;     /* from mla_softmax_scale() */
 
-    /* q_nope [B][H][128], q_pe [B][H][64] (q_pe raw: rotated inside) */
+    /* q_nope [B][H][128], q_pe [B][H][64] (q_pe raw: rotated inside);
+     * strides are multiples of 8 (rows are read 16 bytes at a time) */
     const void* q_nope;  int64_t q_nope_stride_b, q_nope_stride_h;
     const void* q_pe;    int64_t q_pe_stride_b,   q_pe_stride_h;
-    /* w_uk, w_uv [H][128][512], row stride 512, head stride given; passing
-     * wkv_b viewed as [H][256][512] works with w_uv = w_uk + 128*512 and
-     * both head strides 256*512. */
+    /* w_uk, w_uv [H][128][512], row stride 512, head stride given (a
+     * multiple of 8); passing wkv_b viewed as [H][256][512] works with
+     * w_uv = w_uk + 128*512 and both head strides 256*512. */
     const void* w_uk;    int64_t w_uk_stride_h;
     const void* w_uv;    int64_t w_uv_stride_h;
     /* kv_cache [B][max_cache_len][512], pe_cache [B][max_cache_len][64];

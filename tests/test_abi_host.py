@@ -104,6 +104,7 @@ def _params(mla, **kw):
     ("d_nope", 64, 2), ("kv_rank", 256, 2), ("dtype_act", 5, 2),
     ("B", 0, 1), ("K", 0, 1), ("q_nope", 0, 1), ("kv_cache", (1 << 20) + 2, 1),
     ("kv_stride_t", 513, 1), ("pe_stride_t", 32, 1), ("idx_stride_b", 8, 1),
+    ("q_pe_stride_h", 68, 1), ("w_uk_stride_h", 128 * 512 + 4, 1),
     ("softmax_scale", -1.0, 1), ("num_splits", 65, 1), ("flags", 2, 1), ("max_cache_len", 0, 1),
     ("workspace_size", 0, 3),
 ])
