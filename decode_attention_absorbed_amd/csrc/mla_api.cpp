@@ -23,7 +23,7 @@ int fail(int code, const char* fmt, ...) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Largest cache length the selection bitmap supports (LDS holds L_max/8 bytes).
-constexpr int kMaxCacheLen = 1 << 20;
+constexpr int kMaxCacheLen = 1 << 19;
 constexpr int kMaxBatch = 1 << 20;
 constexpr int kMaxHeads = 1 << 12;
 constexpr int kMaxSplits = 64;

@@ -213,7 +213,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // remainder, two MFMAs each, so they enter with ~16 significant bits) and
 // stored row-major in a wave-private LDS region; the MFMA operand (8
 // consecutive features of one column) is then read with ds_read_b64_tr_b16.
-constexpr int ABS_WAVE_LDS = 2 * D_NOPE * 64 * 2;     // two parts x [128][64] bf16
+constexpr int ABS_WAVE_LDS = D_NOPE * 64 * 2;         // one part: [128][64] bf16
 
 template <typename WT>
 __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
@@ -222,60 +222,71 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
     const WT* W = (const WT*)a.w_uk + h * a.wk_sh + c0;
-    char* wl = lds + wave * ABS_WAVE_LDS;             // part pp, row d, column c at pp*16384 + d*128 + c*2 (swizzled)
+    char* wl = lds + wave * ABS_WAVE_LDS;             // row d, column c at d*128 + c*2 (swizzled)
     // Row d holds 64 columns = 8 chunks of 16 bytes; chunk q sits at slot
     // q ^ (d & 7) so that the transposed reads (4 rows x 16 columns per 16
     // lanes) do not collide.
-    auto waddr = [&](int pp, int d, int c) {
-        return pp * (D_NOPE * 128) + d * 128 + ((((c >> 3) ^ (d & 7))) << 4) + (c & 7) * 2;
+    auto waddr = [&](int d, int c) {
+        return d * 128 + ((((c >> 3) ^ (d & 7))) << 4) + (c & 7) * 2;
     };
-    // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i.
-    {
-        const int cq = 4 * (lane & 15);
-#pragma unroll 8
-        for (int i = 0; i < D_NOPE / 4; ++i) {
-            const int d = (lane >> 4) + 4 * i;
-            float v[4];
-            if constexpr (sizeof(WT) == 4) {
-                const f32x4 x = *(const f32x4*)(W + d * RANK + cq);
-                v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-            } else {
-                const bf16x4 x = *(const bf16x4*)(W + d * RANK + cq);
-                v[0] = (float)x[0]; v[1] = (float)x[1]; v[2] = (float)x[2]; v[3] = (float)x[3];
-            }
-            bf16x4 hi, lo;
+    // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i,
+    // all 32 loads in flight at once.
+    const int cq = 4 * (lane & 15);
+    float wv[D_NOPE / 4][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                hi[e] = (bf16)v[e];
-                lo[e] = (bf16)(v[e] - (float)hi[e]);
-            }
-            *(bf16x4*)(wl + waddr(0, d, cq)) = hi;
-            if constexpr (NP == 2) *(bf16x4*)(wl + waddr(1, d, cq)) = lo;
+    for (int i = 0; i < D_NOPE / 4; ++i) {
+        const int d = (lane >> 4) + 4 * i;
+        if constexpr (sizeof(WT) == 4) {
+            const f32x4 x = *(const f32x4*)(W + d * RANK + cq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[i][e] = x[e];
+        } else {
+            const bf16x4 x = *(const bf16x4*)(W + d * RANK + cq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wv[i][e] = (float)x[e];
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xC07F);               // this wave's LDS writes done (only it reads them)
+    // bf16 parts, packed right away so the fp32 values die early
+    bf16x4 wp[NP][D_NOPE / 4];
+#pragma unroll
+    for (int i = 0; i < D_NOPE / 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bf16 hi = (bf16)wv[i][e];
+            wp[0][i][e] = hi;
+            if constexpr (NP == 2) wp[NP - 1][i][e] = (bf16)(wv[i][e] - (float)hi);
+        }
     // Weight operand (A) of K step kb, column block nb: lane l holds column
     // 32 nb + l%32, features 16 kb + 8 (l/32) .. +7 -- two transposed reads of
     // 4 rows each.  In a 16-lane block, lane 4j + q addresses row
     // 16 kb + 8 (blk >> 1) + 4 rr + j, columns 32 nb + 16 (blk & 1) + 4 q .. +3.
     const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
-    auto bop = [&](int pp, int nb, int kb) {
-        bf16x4 r[2];
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int d = 16 * kb + 8 * (blk >> 1) + 4 * rr + jj;
-            const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
-            r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(pp, d, c)));
-        }
-        return cat(r[0], r[1]);
-    };
     bf16x8 bw[NP][2][8];
+    // The parts pass through the wave's LDS region one after the other:
+    // part 0 = bf16(w), part 1 = bf16(w - part 0).  A wave's LDS accesses run
+    // in order, so the second part's writes follow the first part's reads.
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
+    for (int pp = 0; pp < NP; ++pp) {
+#pragma unroll
+        for (int i = 0; i < D_NOPE / 4; ++i) *(bf16x4*)(wl + waddr((lane >> 4) + 4 * i, cq)) = wp[pp][i];
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's writes done (only it reads them)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) bw[pp][nb][kb] = bop(pp, nb, kb);
+            for (int kb = 0; kb < 8; ++kb) {
+                bf16x4 r[2];
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int d = 16 * kb + 8 * (blk >> 1) + 4 * rr + jj;
+                    const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
+                    r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(d, c)));
+                }
+                bw[pp][nb][kb] = cat(r[0], r[1]);
+            }
+        __builtin_amdgcn_s_waitcnt(0xC07F);           // reads done before the next part overwrites
+        asm volatile("" ::: "memory");
+    }
 
     auto load_q = [&](int b0, bf16x8 (&aq)[8]) {
         const int bA = b0 + l32;
@@ -288,14 +299,10 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
             for (int kb = 0; kb < 8; ++kb) aq[kb] = bf16x8{};
         }
     };
-    bf16x8 aqn[8];
-    load_q(0, aqn);
     for (int b0 = 0; b0 < a.B; b0 += 32) {
         const int bA = b0 + l32;
         bf16x8 aq[8];
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) aq[kb] = aqn[kb];
-        if (b0 + 32 < a.B) load_q(b0 + 32, aqn);     // next sequences' queries in flight
+        load_q(b0, aq);
         // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
         // sequence b0 + l%32 and columns 8(i/4) + 4(l/32) + i%4, so each lane
         // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
@@ -340,23 +347,24 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
 // Block bid computes absorption slice bid (head bid/2, half bid%2) when
 // bid < 2H, then the selection and rotary query of sequences bid,
 // bid + gridDim.x, ...  The dynamic LDS serves both parts in turn.
-// LDS of a prep block: the absorption's weight staging (4 waves) and, in
-// turn, the selection bitmap of up to 2^20 positions.
+// LDS of a prep block: the absorption's weight staging (4 waves) or the
+// selection bitmap of up to 2^19 positions.  64 KB lets two blocks share a
+// CU, so selection blocks run beside absorption blocks.
 constexpr int PREP_LDS = 4 * ABS_WAVE_LDS;
-static_assert(PREP_LDS >= (1 << 20) / 8, "bitmap of the largest cache");
+static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 
+// Blocks [0, B) prepare one sequence each (selection, rotary query); blocks
+// [B, B + 2H) compute absorption slice bid - B (head (bid-B)/2, half (bid-B)%2).
 template <typename ActT, typename WT>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
-    __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[PREP_LDS / 4];
+    __shared__ __attribute__((aligned(16))) uint32_t plds[PREP_LDS / 4];
     const int bid = blockIdx.x;
-    if (bid < a.n_absorb) {
-        const int h = bid >> 1, half = bid & 1;
-        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half, (char*)dyn_lds);
+    if (bid < a.B) {
+        prep_sequence<ActT, ActT>(a, bid, plds);
+    } else {
+        const int k = bid - a.B, h = k >> 1, half = k & 1;
+        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half, (char*)plds);
         else absorb_f32<WT>(a, h, half);
-    }
-    for (int b = bid; b < a.B; b += gridDim.x) {
-        __syncthreads();                              // LDS free for the bitmap
-        prep_sequence<ActT, ActT>(a, b, dyn_lds);
     }
 }
 
@@ -371,7 +379,7 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     a.idx = p.topk_indices; a.idx_sb = p.idx_stride_b;
     a.cache_lens = p.cache_lens; a.rope_table = p.rope_table;
     a.qt = w.qt; a.list = w.list; a.counts = w.counts; a.status = w.status;
-    const dim3 grid(a.n_absorb > p.B ? a.n_absorb : p.B), block(256);
+    const dim3 grid(a.n_absorb + p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;
     if (plan.bf16_path) {
         if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float>), grid, block, 0, s, a);

@@ -117,7 +117,7 @@ typedef struct mla_decode_params {
     int32_t d_rope;            /* must be 64  (rotary features per head)  */
     int32_t d_v;               /* must be 128 (value features per head)   */
     int32_t kv_rank;           /* must be 512 (latent rank)               */
-    int32_t max_cache_len;     /* L_max: rows allocated per sequence in the caches */
+    int32_t max_cache_len;     /* L_max: rows allocated per sequence in the caches, 1..2^19 */
     int32_t rope_table_len;    /* rows of rope_table (its T_max) */
     /* dtypes: MLA_DTYPE_BF16 or MLA_DTYPE_F32 */
     int32_t dtype_act;         /* q_nope, q_pe, kv_cache, pe_cache */
