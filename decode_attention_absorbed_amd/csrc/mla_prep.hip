@@ -101,12 +101,93 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_wave) {
 // Selection compaction for sequence b: every position listed in the index
 // row (minus -1 slots and entries outside [0, L_b)), once, ascending.
 // LDS holds a bitmap of ceil(L_max / 32) words.
+// Rotary query of one (head, 32-feature half): x is the raw q_pe slice,
+// t the (cos, sin) pairs of row p_b; writes Q~[b, h, 512 + f0 ..].
+template <typename QtT>
+__device__ __forceinline__ void rotate32(const PrepArgs& a, int b, int h, int f0, const float (&x)[32],
+                                         const float (&t)[32]) {
+    QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f0;
+    QtT y[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float c = t[2 * i], sn = t[2 * i + 1];
+        y[2 * i] = from_f32<QtT>(x[2 * i] * c - x[2 * i + 1] * sn);
+        y[2 * i + 1] = from_f32<QtT>(x[2 * i] * sn + x[2 * i + 1] * c);
+    }
+    if constexpr (sizeof(QtT) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            bf16x8 v;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = y[8 * k + j];
+            *(bf16x8*)(dst + 8 * k) = v;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *(f32x4*)(dst + 4 * k) = f32x4{y[4 * k], y[4 * k + 1], y[4 * k + 2], y[4 * k + 3]};
+    }
+}
+
+template <typename ActT>
+__device__ __forceinline__ void load_qpe32(const PrepArgs& a, int b, int h, int f0, float (&x)[32]) {
+    const ActT* q = (const ActT*)a.q_pe + b * a.qp_sb + h * a.qp_sh + f0;
+    if constexpr (sizeof(ActT) == 2) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bf16x8 v = *(const bf16x8*)(q + 8 * k);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[8 * k + j] = (float)v[j];
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const f32x4 v = *(const f32x4*)(q + 4 * k);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x[4 * k + j] = v[j];
+        }
+    }
+}
+
+// One sequence: the rotary query at p_b = L_b - 1 (pairs (2i, 2i+1) are one
+// complex number) and the selection compaction (every position listed in
+// the index row, minus -1 slots and entries outside [0, L_b), once,
+// ascending).  LDS holds a bitmap of ceil(L_b / 32) words.  The global
+// loads that do not depend on each other (cache length, the first 2048
+// indices, the first q_pe slices) are issued together up front.
 template <typename QtT, typename ActT>
 __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     __shared__ int lds_wave[4];
     __shared__ uint32_t lds_status;
     const int tid = threadIdx.x;
+    const int32_t* row = a.idx + (long long)b * a.idx_sb;
+    const bool vec = ((uintptr_t)row & 15) == 0;
+    const int kv = vec ? (a.K & ~3) : 0;              // indices read four at a time
+    // -- loads issued together --
     const int L = a.cache_lens[b];
+    int4 iv[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int j = 4 * tid + 1024 * k;
+        iv[k] = j < kv ? *(const int4*)(row + j) : int4{-1, -1, -1, -1};
+    }
+    float x[32];
+    const bool rot0 = tid < 2 * a.H;                  // this thread's first (head, half)
+    if (rot0) load_qpe32<ActT>(a, b, tid >> 1, 32 * (tid & 1), x);
+    // -- rotary query --
+    const int p = min(max(L - 1, 0), a.Trope - 1);
+    const float* cs = a.rope_table + (long long)p * D_ROPE;
+    for (int e = tid; e < a.H * 2; e += 256) {
+        const int h = e >> 1, f0 = 32 * (e & 1);
+        if (e != tid) load_qpe32<ActT>(a, b, h, f0, x);
+        float t[32];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const f32x4 v = *(const f32x4*)(cs + f0 + 4 * k);
+            t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
+        }
+        rotate32<QtT>(a, b, h, f0, x, t);
+    }
+    // -- selection --
     uint32_t status = 0;
     if (L < 1 || L > a.Lmax || L > a.Trope) status |= BAD_CACHE_LEN;
     const int Lc = L < 0 ? 0 : (L > a.Lmax ? a.Lmax : L);
@@ -114,7 +195,6 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     if (tid == 0) lds_status = 0;
     for (int w = tid; w < nwords; w += 256) bm[w] = 0u;
     __syncthreads();
-    const int32_t* row = a.idx + (long long)b * a.idx_sb;
     auto mark = [&](int v) {
         if (v == -1) return;
         if (v < 0 || v >= L) { status |= BAD_INDEX_RANGE; return; }
@@ -127,10 +207,11 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
             __hip_atomic_fetch_or(&bm[v >> 5], bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     };
-    // four indices per thread and step when the row is 16-byte aligned
-    const bool vec = ((uintptr_t)row & 15) == 0;
-    const int kv = vec ? (a.K & ~3) : 0;
-    for (int j = 4 * tid; j < kv; j += 1024) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        mark(iv[k].x); mark(iv[k].y); mark(iv[k].z); mark(iv[k].w);
+    }
+    for (int j = 4 * tid + 2048; j < kv; j += 1024) {
         const int4 v = *(const int4*)(row + j);
         mark(v.x); mark(v.y); mark(v.z); mark(v.w);
     }
@@ -154,51 +235,6 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     if (tid == 0) {
         a.counts[b] = total;
         if (total == 0) status |= BAD_EMPTY;
-    }
-    // Rotary query at p_b = L_b - 1: pairs (2i, 2i+1) are one complex number.
-    // Thread t rotates head t/2, features 32 (t%2) .. +31 (16 pairs).
-    const int p = min(max(L - 1, 0), a.Trope - 1);
-    const float* cs = a.rope_table + (long long)p * D_ROPE;
-    for (int e = tid; e < a.H * 2; e += 256) {
-        const int h = e >> 1, f0 = 32 * (e & 1);
-        const ActT* q = (const ActT*)a.q_pe + b * a.qp_sb + h * a.qp_sh + f0;
-        float x[32], t[32];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if constexpr (sizeof(ActT) == 2) {
-                const bf16x8 v = *(const bf16x8*)(q + 8 * k);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[8 * k + j] = (float)v[j];
-            } else {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) x[8 * k + j] = to_f32(q[8 * k + j]);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const f32x4 v = *(const f32x4*)(cs + f0 + 4 * k);
-            t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
-        }
-        QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f0;
-        QtT y[32];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float c = t[2 * i], sn = t[2 * i + 1];
-            y[2 * i] = from_f32<QtT>(x[2 * i] * c - x[2 * i + 1] * sn);
-            y[2 * i + 1] = from_f32<QtT>(x[2 * i] * sn + x[2 * i + 1] * c);
-        }
-        if constexpr (sizeof(QtT) == 2) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                bf16x8 v;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) v[j] = y[8 * k + j];
-                *(bf16x8*)(dst + 8 * k) = v;
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 32; ++i) dst[i] = y[i];
-        }
     }
     if (status) atomicOr(&lds_status, status);
     __syncthreads();
@@ -299,10 +335,14 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
             for (int kb = 0; kb < 8; ++kb) aq[kb] = bf16x8{};
         }
     };
+    bf16x8 aqn[8];
+    load_q(0, aqn);
     for (int b0 = 0; b0 < a.B; b0 += 32) {
         const int bA = b0 + l32;
         bf16x8 aq[8];
-        load_q(b0, aq);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) aq[kb] = aqn[kb];
+        if (b0 + 32 < a.B) load_q(b0 + 32, aqn);     // next sequences' queries in flight
         // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
         // sequence b0 + l%32 and columns 8(i/4) + 4(l/32) + i%4, so each lane
         // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
