@@ -69,81 +69,102 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
         }
     }
 
-    for (int b0 = 0; b0 < a.B; b0 += 32) {
-        const int bA = b0 + l32;
-        f32x16 acc[2] = {f32x16{}, f32x16{}};
-        float M = -INFINITY, Wsum = 0.f;
-        // A operand: the merged latent of sequence bA over this wave's 64
-        // columns (zero past the batch); splits are taken four at a time so
-        // that their loads are in flight together.  The MFMAs below run with
-        // every lane active.
-        bf16x8 av[MKB];
+    // The partials are consumed in units of (32 sequences, 2 splits); unit
+    // u + 1 is loaded while unit u is processed, across the reduction of a
+    // finished batch too, so the memory system never idles between batches.
+    // Splits are combined with a running maximum (rescaling what was summed
+    // when the maximum grows).
+    const int G = (a.S + 1) / 2;                     // split pairs per sequence
+    const int U = ((a.B + 31) / 32) * G;
+    auto load_unit = [&](int u, bf16x8 (&v)[2][MKB], float (&ls)[2]) {
+        const int bA = 32 * (u / G) + l32, s0 = 2 * (u % G);
 #pragma unroll
-        for (int kb = 0; kb < MKB; ++kb) av[kb] = bf16x8{};
-        if (bA < a.B) {
-            const float* ls = a.lsepart + (long long)bA * a.S * a.H + h;
-            for (int s = 0; s < a.S; ++s) M = fmaxf(M, ls[(long long)s * a.H]);
-            float xs[MKB][8];
+        for (int t = 0; t < 2; ++t) {
+            const int s = s0 + t;
+            const bool ok = bA < a.B && s < a.S;
+            const long long row = ((long long)bA * a.S + s) * a.H + h;
+            ls[t] = ok ? a.lsepart[row] : -INFINITY;
+            const bf16* src = a.opart + row * RANK + col0 + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < MKB; ++kb) v[t][kb] = ok ? *(const bf16x8*)(src + 16 * kb) : bf16x8{};
+        }
+    };
+    bf16x8 vc[2][MKB], vn[2][MKB];
+    float lc[2], ln[2];
+    load_unit(0, vc, lc);
+    float M = -INFINITY, Wsum = 0.f;
+    float xs[MKB][8];
+#pragma unroll
+    for (int kb = 0; kb < MKB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) load_unit(u + 1, vn, ln);
+        // fold the current unit's two splits into the running sums
+        const float Mn = fmaxf(M, fmaxf(lc[0], lc[1]));
+        const float sc = M == Mn ? 1.f : exp2f(M - Mn);
+        const float w0 = exp2f(lc[0] - Mn), w1 = exp2f(lc[1] - Mn);
+        Wsum = Wsum * sc + w0 + w1;
+#pragma unroll
+        for (int kb = 0; kb < MKB; ++kb)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                xs[kb][j] = fmaf(w1, (float)vc[1][kb][j], fmaf(w0, (float)vc[0][kb][j], xs[kb][j] * sc));
+        M = Mn;
+        if (u % G == G - 1) {
+            // batch of 32 sequences complete: A operand = merged latent (bf16,
+            // zero past the batch), MFMAs with every lane active, reduction
+            // over the 8 waves' column ranges, output
+            const int b0 = 32 * (u / G), bA = b0 + l32;
+            const float invW = 1.f / Wsum;
+            bf16x8 av[MKB];
+#pragma unroll
+            for (int kb = 0; kb < MKB; ++kb)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) av[kb][j] = bA < a.B ? f2bf(xs[kb][j] * invW) : (bf16)0.f;
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int kb = 0; kb < MKB; ++kb)
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
+            if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
+                a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
+            __syncthreads();                        // previous batch's reads of red[] done
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) red[((wave * 2 + nb) * 16 + i) * 64 + lane] = acc[nb][i];
+            __syncthreads();
+            // 32 sequences x 64 outputs; D element (row 8(i/4) + 4gg + i%4,
+            // column 32 nb + n) sits at red[w][nb][i][32 gg + n]
+#pragma unroll
+            for (int k = 0; k < 2048 / (64 * MW); ++k) {
+                const int e = tid + 64 * MW * k;
+                const int dl = e & 63, bl = e >> 6;
+                const int nb = dl >> 5, n = dl & 31;
+                const int i = 4 * (bl >> 3) + (bl & 3), gg = (bl >> 2) & 1;
+                const int lnn = gg * 32 + n;
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < MW; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + lnn];
+                const int bo = b0 + bl;
+                if (bo < a.B)
+                    ((OutT*)a.out)[bo * a.out_sb + h * a.out_sh + 64 * dh + dl] = from_f32<OutT>(v);
+            }
+            M = -INFINITY;
+            Wsum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < MKB; ++kb)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
-            const bf16* src0 = a.opart + ((long long)bA * a.S * a.H + h) * RANK + col0 + 8 * g;
-            for (int s0 = 0; s0 < a.S; s0 += 4) {
-                bf16x8 v[4][MKB];
-                float ws[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int s = s0 + u;
-                    ws[u] = s < a.S ? exp2f(ls[(long long)s * a.H] - M) : 0.f;
-#pragma unroll
-                    for (int kb = 0; kb < MKB; ++kb)
-                        v[u][kb] = s < a.S ? *(const bf16x8*)(src0 + (long long)s * a.H * RANK + 16 * kb) : bf16x8{};
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    Wsum += ws[u];
-#pragma unroll
-                    for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) xs[kb][j] = fmaf(ws[u], (float)v[u][kb][j], xs[kb][j]);
-                }
-            }
-            const float invW = 1.f / Wsum;
-#pragma unroll
-            for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) av[kb][j] = f2bf(xs[kb][j] * invW);
         }
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int t = 0; t < 2; ++t) {
+            lc[t] = ln[t];
 #pragma unroll
-            for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
-        if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
-            a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
-        __syncthreads();                        // previous step's reads of red[] done
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red[((wave * 2 + nb) * 16 + i) * 64 + lane] = acc[nb][i];
-        __syncthreads();
-        // 32 sequences x 64 outputs; D element (row 8(i/4) + 4gg + i%4, column
-        // 32 nb + n) sits at red[w][nb][i][32 gg + n]
-#pragma unroll
-        for (int k = 0; k < 2048 / (64 * MW); ++k) {
-            const int e = tid + 64 * MW * k;
-            const int dl = e & 63, bl = e >> 6;
-            const int nb = dl >> 5, n = dl & 31;
-            const int i = 4 * (bl >> 3) + (bl & 3), gg = (bl >> 2) & 1;
-            const int ln = gg * 32 + n;
-            float v = 0.f;
-#pragma unroll
-            for (int w = 0; w < MW; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + ln];
-            const int bo = b0 + bl;
-            if (bo < a.B)
-                ((OutT*)a.out)[bo * a.out_sb + h * a.out_sh + 64 * dh + dl] = from_f32<OutT>(v);
+            for (int kb = 0; kb < MKB; ++kb) vc[t][kb] = vn[t][kb];
         }
     }
 }
