@@ -24,8 +24,15 @@
 //         QK^T accumulator: the rows of the contraction are ordered to match
 //         the accumulator layout, and V^T is read in that order with
 //         ds_read_b64_tr_b16.  O^T lives in the 256 AGPRs.
-// No wave waits for another's softmax, so QK^T and PV read the same stage
-// and three tiles are in flight while one is consumed.
+//
+// With one wave per SIMD a wave issues at most one instruction every few
+// cycles, so the tile loop is written to keep its instruction count well
+// under the MFMA time (68 MFMAs of 32 cycles per tile): every LDS operand
+// address is a per-lane base plus an immediate offset, the copies of a tile
+// cost the same number of instructions whether its rows exist or not (rows
+// past the split read outside the buffer window and land as zeros), so the
+// copy wait is one constant count, and only the first and the last tile
+// take a (uniform) branch.
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
 
@@ -47,27 +54,41 @@ struct AttnArgs {
 constexpr int HW = 128;                // heads per workgroup
 constexpr int R = 32;                  // rows per tile
 constexpr int NST = 4;                 // LDS stages
-constexpr int LAT = R * RANK * 2;      // latent region of a stage: row r at r * 1 KB
-constexpr int STAGE = R * ROW * 2;     // + rotary region: row r at LAT + r * 128
+
+// Latent region of a stage.  Tile row m (the MFMA row index) is stored
+// unswizzled, 1 KB at row_start(m), and the row starts are shifted against
+// each other within the 256-byte bank window:
+//   shift(m) = 64 (m & 3) + 16 ((m >> 2) & 3),
+//   row_start(m) = 1024 (2 (shift(m) / 16) + m / 16) + shift(m),
+// i.e. the rows sit in order of increasing shift, two per shift value, so
+// the whole region is only 240 bytes larger than 32 KB.  The LDS serves 16
+// lanes of a 16-byte read or 32 lanes of an 8-byte read per cycle:
+//   QK^T operand read (lanes 0..15 = rows 0..15 at one chunk): 16 distinct
+//     shifts, 16 distinct 16-byte slots;
+//   transposed PV read (lanes 0..31 = rows 4q..4q+3, 64 bytes each): shifts
+//     64 j + 16 (q & 3), j = 0..3, four disjoint 64-byte windows.
+// A step's offset within a row (32 bytes per QK^T step, 64 bytes per PV
+// column block) is then an immediate on a per-lane base.
+__host__ __device__ constexpr int row_shift(int m) { return 64 * (m & 3) + 16 * ((m >> 2) & 3); }
+__host__ __device__ constexpr int row_start(int m) { return 1024 * (2 * (row_shift(m) >> 4) + (m >> 4)) + row_shift(m); }
+constexpr int LATB = 33024;            // >= row_start(31) + 1024 = 33008, 256-aligned
+static_assert(row_start(31) + 1024 <= LATB, "latent region");
+// Rotary region: row m at LATB + 128 m, its 16-byte chunk c' (0..7) at slot
+// c' ^ ((m >> 1) & 7); 16 consecutive rows at one chunk hit 16 distinct slots.
+constexpr int STAGE = LATB + R * 128;
 constexpr int NSLOT = 4;               // index ring slots
-constexpr int OFF_IDX = NST * STAGE;               // [NSLOT][4 waves][8] int: row indices
+constexpr int OFF_IDX = NST * STAGE;                // [NSLOT][4 waves][8] int: row indices (1-based)
 constexpr int OFF_FLAG = OFF_IDX + NSLOT * 4 * 8 * 4;
-constexpr int QK_REG = 33;                         // Q~ feature blocks 0..32 live in registers,
-constexpr int QK_LDS = ROW / 16 - QK_REG;          // blocks 33..35 in LDS: [block][head][16]
+constexpr int QK_REG = 33;                          // Q~ feature blocks 0..32 live in registers,
+constexpr int QK_LDS = ROW / 16 - QK_REG;           // blocks 33..35 in LDS: [block][head][16]
 constexpr int OFF_Q = OFF_FLAG + 16;
-constexpr int QK_DEPTH = 4;                        // QK^T operand reads run this many steps ahead
-constexpr int PV_DEPTH = 4;                        // PV operand reads run this many steps ahead
+constexpr int QK_DEPTH = 4;                         // QK^T operand reads run this many steps ahead
+constexpr int PV_DEPTH = 4;                         // PV operand reads run this many steps ahead
 constexpr int LDS_BYTES = OFF_Q + QK_LDS * HW * 32;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-
-// Tile layout in LDS.  Latent region: row r at r * 1024 bytes, its 16-byte
-// chunk c (8 latent features) at slot c ^ swz(r), with the 5-bit swizzle
-// swz(r) = ((r&3)<<2) | ((r>>2)&3) | (r&16), a bijection on the 32 rows of a
-// tile.  The LDS serves 32 lanes per cycle: the QK^T operand read (32 rows at
-// one chunk) then touches 32 distinct 16-byte slots, and each half of a
-// transposed PV read (4 rows x 4 chunks) 16 distinct slots.
-// Rotary region: row r at r * 128 bytes, chunk c' (0..7) at slot c' ^ ((r>>1)&7).
-__device__ __forceinline__ int lat_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3) | (r & 16); }
+static_assert(STAGE % 256 == 0 && OFF_Q % 16 == 0, "alignment");
+// Copies per wave per tile: one index fetch, 8 latent rows, one rotary copy.
+constexpr int COPIES_PER_TILE = 10;
 
 // The wave index, known to the compiler as wave-uniform (an SGPR).
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
@@ -75,21 +96,6 @@ __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane
 // Largest exponent (log2) a probability may reach relative to the
 // reference maximum before the split is recomputed with the exact maximum.
 constexpr float P_EXP_LIMIT = 64.f;
-
-// s_waitcnt vmcnt(n) for the counts the copy pipeline produces (n is
-// rounded down to one of them, which only waits longer).
-__device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 53) wait_vmcnt<53>();
-    else if (n >= 52) wait_vmcnt<52>();
-    else if (n >= 51) wait_vmcnt<51>();
-    else if (n >= 42) wait_vmcnt<42>();
-    else if (n >= 33) wait_vmcnt<33>();
-    else if (n >= 20) wait_vmcnt<20>();
-    else if (n >= 19) wait_vmcnt<19>();
-    else if (n >= 18) wait_vmcnt<18>();
-    else if (n >= 9) wait_vmcnt<9>();
-    else wait_vmcnt<0>();
-}
 
 // Workgroup barrier for the main loop.  It waits for this wave's LDS
 // operations only: the buffer->LDS copies still in flight target stages no
@@ -102,72 +108,68 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Keeps the compiler from hoisting per-read address arithmetic out of the
-// tile loop (which would hold one register per distinct address) or turning
-// lane-dependent loop terms into induction variables that live in VGPRs
-// across the whole kernel.
+// tile loop (which would hold one register per distinct address).
 __device__ __forceinline__ void opaque(int& x) { asm volatile("" : "+v"(x)); }
 
 struct SplitCtx {
     int b, s, h0, start, end, ntiles;
-    rsrc_t list;        // the sequence's compacted row list
+    rsrc_t list;        // this split's part of the compacted row list
     rsrc_t kv;          // the sequence's rows of the latent cache
     rsrc_t pe;          // the sequence's rows of the rotary-key cache
 };
 
-// Per-lane LDS offsets.  The swizzles are XORs on address bits that the
-// bases leave zero, so every operand address is a base XOR a constant.
-//   QK latent chunk 16j + 2k + lane/32 of row lane%32:  qk ^ (k << 5) ^ (j << 8)
-//   QK rotary chunk 2k + lane/32:                       rot ^ (k << 5)
-//   PV read rd of column block cb (32 columns), rows 16 kt + 8 rd + 4 (lane/32) + 0..3:
-//                                                       (tr[rd] ^ ((cb & 3) << 6)) + 256 ((cb >> 2) ^ kt) + 16384 kt
-//   Q~ block 33 + i (LDS part):                         q + 4096 i
+// Per-lane constants.
+//   qk:  QK^T latent operand of step ks (< 32): qk + stage + 32 ks
+//   rot: QK^T rotary operand of step 32 + k:    (rot ^ (k << 5)) + stage
+//   tr:  PV read rd (rows 16 kt + 8 rd + 4 (lane/32) + 0..3) of column
+//        block cb:                              tr[rd] + stage + 1024 kt + 64 cb
+//   q:   Q~ block 33 + i (LDS part):            q + 4096 i
+//   lat: byte offset in a latent row for this lane's copy, minus one row
+//        stride (the row list is 1-based)
+//   rcp: the same for the rotary copy
 struct LaneOffsets {
     int qk, rot, tr[2], q;
+    uint32_t lat, rcp;
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets() {
+__device__ __forceinline__ LaneOffsets lane_offsets(const AttnArgs& a) {
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int g = lane >> 5, l32 = lane & 31;
     LaneOffsets lo;
-    // chunk (16j + 2k + g) ^ sw of row l32: bit 0 is g ^ (sw & 1), bits 1-3
-    // are k ^ ((sw >> 1) & 7), bits 4-5 are j ^ (sw >> 4)
-    const int sw = lat_swz(l32);
-    lo.qk = l32 * 1024 + ((g ^ (sw & 1)) << 4) + (((sw >> 1) & 7) << 5) + ((sw >> 4) << 8);
+    lo.qk = row_start(l32) + 16 * g;
+    // chunk 2k + g of rotary row l32 sits at slot (2k + g) ^ u: bit 0 is
+    // g ^ (u & 1), bits 1-2 are k ^ (u >> 1)
     const int u = (l32 >> 1) & 7;
-    lo.rot = LAT + l32 * 128 + ((g ^ (u & 1)) << 4) + ((u >> 1) << 5);
+    lo.rot = LATB + l32 * 128 + ((g ^ (u & 1)) << 4) + ((u >> 1) << 5);
     // Transposed reads: in 16-lane block blk, lane 4j + qq addresses row
-    // 16 kt + 8 rd + 4 (blk >> 1) + j, columns 16 (blk & 1) + 4 qq .. +3 of the
-    // column block; lane i of the block receives column 16 (blk & 1) + i of
-    // the rows 16 kt + 8 rd + 4 (blk >> 1) + 0..3.  The row's swizzle has bits
-    // 2-3 = j, bits 0-1 = (2 rd + (blk >> 1)) & 3 and bit 4 = kt.
+    // 8 rd + 4 (blk >> 1) + j (+16 kt), columns 16 (blk & 1) + 4 qq .. +3 of
+    // the column block; lane i of the block receives column 16 (blk & 1) + i
+    // of the rows 8 rd + 4 (blk >> 1) + 0..3.
     const int blk = lane >> 4, L = lane & 15, j = L >> 2, qq = L & 3;
 #pragma unroll
-    for (int rd = 0; rd < 2; ++rd) {
-        const int lowsw = (2 * rd + (blk >> 1)) & 3;
-        lo.tr[rd] = (8 * rd + 4 * (blk >> 1) + j) * 1024 + (((2 * (blk & 1) + (qq >> 1)) ^ lowsw) << 4) +
-                    (qq & 1) * 8 + (j << 6);
-    }
+    for (int rd = 0; rd < 2; ++rd)
+        lo.tr[rd] = row_start(8 * rd + 4 * (blk >> 1) + j) + 32 * (blk & 1) + 8 * qq;
     lo.q = OFF_Q + (wave * 32 + l32) * 32 + 16 * g;
+    lo.lat = (uint32_t)lane * 16u - (uint32_t)a.kv_st * 2u;
+    // rotary copy: lane l fills slot l & 7 of row 8 wave + l/8, i.e. chunk
+    // (l & 7) ^ ((row >> 1) & 7) of that row
+    const int rrow = wave * 8 + (lane >> 3);
+    lo.rcp = (uint32_t)(((lane & 7) ^ ((rrow >> 1) & 7)) << 4) - (uint32_t)a.pe_st * 2u;
     return lo;
 }
 
 // Row indices of tile T for this wave: lanes 0..7 copy 4 bytes each into the
-// ring slot (positions past the end repeat the last row, so every tile costs
-// the same number of copies).
+// ring slot.  The list descriptor's window is the split's rows, so positions
+// past its end read 0 ("no row").
 __device__ __forceinline__ void fetch_idx(const SplitCtx& sc, int T, int* __restrict__ slot) {
     const int lane = threadIdx.x & 63, wave = wave_id();
-    if (lane < 8) {
-        int lp = wave * 8 + lane;
-        opaque(lp);
-        const int pos = min(sc.start + T * R + lp, sc.end - 1);
-        buffer_to_lds4(sc.list, (uint32_t)pos * 4u, (MLA_LDS void*)slot);
-    }
+    if (lane < 8) buffer_to_lds4(sc.list, (uint32_t)(T * R + wave * 8 + lane) * 4u, (MLA_LDS void*)slot);
 }
 
 // Row indices of one tile for this wave, read from its ring slot.
 struct TileRows {
     u32x4 i0, i1;       // rows 8 wave + 0..7 (latent copies)
-    int rot;            // row 8 wave + lane/8 (rotary copy)
+    uint32_t rot;       // row 8 wave + lane/8 (rotary copy)
 };
 
 __device__ __forceinline__ TileRows read_rows(const int* __restrict__ slot) {
@@ -175,50 +177,48 @@ __device__ __forceinline__ TileRows read_rows(const int* __restrict__ slot) {
     TileRows tr;
     tr.i0 = *(const u32x4*)slot;
     tr.i1 = *(const u32x4*)(slot + 4);
-    tr.rot = slot[lane >> 3];
+    tr.rot = (uint32_t)slot[lane >> 3];
     return tr;
 }
 
 // Copy row j (0..7) of this wave's 8 rows of a tile into a stage: 1 KB, lane
-// l moves chunk l ^ swz(r), which lands in slot l.
-__device__ __forceinline__ void issue_row(const AttnArgs& a, const SplitCtx& sc, char* __restrict__ stage,
-                                          const TileRows& tr, int j) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int r = wave * 8 + j;
+// l moves bytes 16 l..16 l+15.  Row index t is 1-based; t = 0 gives an offset
+// far outside the buffer window, and the copy writes zeros.
+__device__ __forceinline__ void issue_row(const AttnArgs& a, const SplitCtx& sc, const LaneOffsets& lo,
+                                          MLA_LDS char* __restrict__ dst, const TileRows& tr, int j) {
     const uint32_t t = __builtin_amdgcn_readfirstlane(j < 4 ? tr.i0[j & 3] : tr.i1[j & 3]);
-    buffer_to_lds16(sc.kv, t * (uint32_t)a.kv_st * 2u + ((lane ^ lat_swz(r)) << 4), (MLA_LDS void*)(stage + r * 1024));
+    buffer_to_lds16(sc.kv, lo.lat + t * ((uint32_t)a.kv_st * 2u), (MLA_LDS void*)dst);
 }
 
 // Copy the rotary parts (128 bytes each) of this wave's 8 rows.
-__device__ __forceinline__ void issue_rot(const AttnArgs& a, const SplitCtx& sc, char* __restrict__ stage,
-                                          const TileRows& tr) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int r = wave * 8 + (lane >> 3);
-    buffer_to_lds16(sc.pe, (uint32_t)tr.rot * (uint32_t)a.pe_st * 2u + (((lane & 7) ^ ((r >> 1) & 7)) << 4),
-                    (MLA_LDS void*)(stage + LAT + wave * 8 * 128));
+__device__ __forceinline__ void issue_rot(const AttnArgs& a, const SplitCtx& sc, const LaneOffsets& lo,
+                                          MLA_LDS char* __restrict__ stage, const TileRows& tr) {
+    const int wave = wave_id();
+    buffer_to_lds16(sc.pe, lo.rcp + tr.rot * ((uint32_t)a.pe_st * 2u), (MLA_LDS void*)(stage + LATB + wave * 1024));
 }
 
 // All 9 copies of this wave's part of a tile (prologue).
-__device__ __forceinline__ void issue_tile(const AttnArgs& a, const SplitCtx& sc, char* __restrict__ stage,
-                                           const int* __restrict__ slot) {
+__device__ __forceinline__ void issue_tile(const AttnArgs& a, const SplitCtx& sc, const LaneOffsets& lo,
+                                           const int (&mst)[8], MLA_LDS char* stage, const int* __restrict__ slot) {
     const TileRows tr = read_rows(slot);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) issue_row(a, sc, stage, tr, j);
-    issue_rot(a, sc, stage, tr);
+    for (int j = 0; j < 8; ++j) issue_row(a, sc, lo, stage + mst[j], tr, j);
+    issue_rot(a, sc, lo, stage, tr);
 }
 
 // v_mfma_f32_32x32x16_bf16 with the accumulator pinned to VGPRs.  The 256
 // AGPRs hold the PV accumulators; if the compiler also placed this chain's
 // accumulator there it would have to move PV accumulators out and back every
-// tile.  The compiler does not track MFMA hazards across inline asm, so the
-// wait states are explicit: "s_nop 1" covers a VALU write of an operand just
-// before the MFMA, and qk_settle pads 21 wait states between the last MFMA
-// (16 passes) and any other read of its result.
+// tile.  Operands come from LDS reads or registers loaded before the loop
+// (no VALU write precedes them), and consecutive MFMAs of the chain use the
+// same accumulator, which the hardware forwards.  The compiler does not
+// track MFMA hazards across inline asm, so qk_settle pads 21 wait states
+// between the last MFMA and any other read of its result.
 __device__ __forceinline__ void qk_mfma_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_mfma(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-    asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_settle(f32x16& acc) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(acc));
@@ -226,64 +226,78 @@ __device__ __forceinline__ void qk_settle(f32x16& acc) {
 
 // QK^T of one tile for this wave's 32 heads: S^T[32 rows][32 heads] in acc
 // (lane l: head l%32, rows 8(i/4) + 4(l/32) + i%4 for i = 0..15); tile
-// operands are read two steps ahead of the MFMAs.  hook(ks) runs after the
-// MFMA of step ks: the copies for a later tile are spread over the chain so
-// that a stalled copy issue never leaves the matrix unit idle for long.
+// operands are read QK_DEPTH steps ahead of the MFMAs.  hook(ks) runs after
+// the MFMA of step ks: the copies for a later tile are spread over the chain.
 template <typename Hook>
 __device__ __forceinline__ void qk_tile(const char* __restrict__ st, const char* __restrict__ smem_q,
-                                        LaneOffsets lo, const bf16x8 (&qreg)[QK_REG], f32x16& acc, Hook&& hook) {
-    opaque(lo.qk);
-    opaque(lo.rot);
+                                        const LaneOffsets& lo, const bf16x8 (&qreg)[QK_REG], f32x16& acc,
+                                        Hook&& hook) {
+    int base = lo.qk, rbase = lo.rot, qb = lo.q;
+    opaque(base);
+    opaque(rbase);
+    opaque(qb);
     constexpr int NK = ROW / 16, D = QK_DEPTH;
-    auto off = [&](int ks) { return ks < 32 ? lo.qk ^ (((ks & 7) << 5) | ((ks >> 3) << 8)) : lo.rot ^ ((ks - 32) << 5); };
     bf16x8 kv[D + 1], qv[D + 1];
     auto load = [&](int ks) {
-        kv[ks % (D + 1)] = *(const bf16x8*)(st + off(ks));
-        if (ks >= QK_REG) qv[ks % (D + 1)] = *(const bf16x8*)(smem_q + lo.q + 4096 * (ks - QK_REG));
+        const int addr = ks < 32 ? base + 32 * ks : (ks == 32 ? rbase : rbase ^ ((ks - 32) << 5));
+        kv[ks % (D + 1)] = *(const bf16x8*)(st + addr);
+        if (ks >= QK_REG) qv[ks % (D + 1)] = *(const bf16x8*)(smem_q + qb + 4096 * (ks - QK_REG));
     };
 #pragma unroll
     for (int ks = 0; ks < D; ++ks) load(ks);
-    // two interleaved chains (even and odd feature blocks): a single
-    // dependent chain runs at the MFMA latency, two at its throughput
-    f32x16 acc1;
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
         if (ks + D < NK) load(ks + D);
         const bf16x8 q = ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks % (D + 1)];
         const bf16x8 k = kv[ks % (D + 1)];
         if (ks == 0) qk_mfma_first(acc, k, q);
-        else if (ks == 1) qk_mfma_first(acc1, k, q);
-        else if (ks & 1) qk_mfma(acc1, k, q);
         else qk_mfma(acc, k, q);
         hook(ks);
         __builtin_amdgcn_sched_barrier(0);
     }
     qk_settle(acc);
-    qk_settle(acc1);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] += acc1[i];
+}
+
+// max(m, x[0..15]) as eight v_max3_f32.  fmaxf on values the compiler
+// cannot prove canonical (results of the inline-asm MFMAs) costs an extra
+// NaN-quieting max per operand.
+__device__ __forceinline__ float max17_raw(float m, const f32x16& x) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3\n\t"
+        "v_max3_f32 %0, %0, %4, %5\n\t"
+        "v_max3_f32 %0, %0, %6, %7\n\t"
+        "v_max3_f32 %0, %0, %8, %9\n\t"
+        "v_max3_f32 %0, %0, %10, %11\n\t"
+        "v_max3_f32 %0, %0, %12, %13\n\t"
+        "v_max3_f32 %0, %0, %14, %15\n\t"
+        "v_max3_f32 %0, %0, %16, %17"
+        : "=&v"(r)
+        : "v"(m), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+          "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+    return r;
 }
 
 // Softmax state of this lane's head (half of its rows: the other half is in
 // lane ^ 32) and the O^T accumulators of the wave's 32 heads.
 struct PassState {
-    float m_ref, m_true, lsum;
+    float m_ref;        // reference maximum (log2 units)
+    float mraw;         // largest raw score (before scaling) seen
+    float lsum;
     f32x16 o[16];       // [cb]: columns 32cb + 8(i/4) + 4(lane/32) + i%4 of head lane%32
 };
 
 // Probabilities of accumulator entries 8kt .. 8kt+7 (rows 16kt + 8(e/4) +
-// 4(lane/32) + e%4): scale, mask rows past the end, exponentiate against the
-// reference maximum; returned as the PV B operand of K step kt.
-__device__ __forceinline__ bf16x8 soft8(PassState& ps, const f32x16& acc, int kt, int rem, float scale_log2) {
+// 4(lane/32) + e%4), exponentiated against the reference maximum (no clamp:
+// a probability that overflows means the split is recomputed, see
+// attn_pass); p keeps them in fp32 for the running sum, the return value is
+// the PV B operand of K step kt.
+__device__ __forceinline__ bf16x8 soft8(const f32x16& acc, int kt, float m_ref, float scale_log2, float (&p)[16]) {
     bf16x8 pk;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int i = 8 * kt + e;
-        const float x = 8 * (i >> 2) + (i & 3) < rem ? acc[i] * scale_log2 : -INFINITY;
-        ps.m_true = fmaxf(ps.m_true, x);
-        const float p = __builtin_amdgcn_exp2f(fminf(x - ps.m_ref, P_EXP_LIMIT));
-        ps.lsum += p;
-        pk[e] = f2bf(p);
+        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m_ref));
+        pk[e] = f2bf(p[i]);
     }
     return pk;
 }
@@ -292,31 +306,76 @@ __device__ __forceinline__ bf16x8 soft8(PassState& ps, const f32x16& acc, int kt
 // two K steps of 16 rows.  The K index k = 8 (lane/32) + e of step kt is row
 // 16kt + 8(e/4) + 4(lane/32) + e%4, matching soft8's operand; the A operand
 // (columns x those rows) is two transposed reads of 4 rows each.  The second
-// K step's probabilities are computed while the first step's MFMAs run.
-__device__ __forceinline__ void pv_tile(const char* __restrict__ st, LaneOffsets lo, PassState& ps,
-                                        const f32x16& acc, int rem, float scale_log2) {
-    opaque(lo.tr[0]);
-    opaque(lo.tr[1]);
+// K step's probabilities are computed while the first step's MFMAs run, the
+// running sum and maximum after them.
+__device__ __forceinline__ void pv_tile(const char* __restrict__ st, const LaneOffsets& lo,
+                                        PassState& ps, const f32x16& acc, float scale_log2) {
+    int t0 = lo.tr[0], t1 = lo.tr[1];
+    opaque(t0);
+    opaque(t1);
     auto tr = [&](int kt, int cb) {
-        const int o = 256 * ((cb >> 2) ^ kt) + 16384 * kt;
-        const bf16x4 r0 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[0] ^ ((cb & 3) << 6)) + o));
-        const bf16x4 r1 = lds_read_tr16((const MLA_LDS void*)(st + (lo.tr[1] ^ ((cb & 3) << 6)) + o));
+        const int o = 1024 * kt + 64 * cb;
+        const bf16x4 r0 = lds_read_tr16((const MLA_LDS void*)(st + t0 + o));
+        const bf16x4 r1 = lds_read_tr16((const MLA_LDS void*)(st + t1 + o));
         return cat(r0, r1);
     };
     constexpr int D = PV_DEPTH;
     bf16x8 av[D + 1];
 #pragma unroll
-    for (int st2 = 0; st2 < D; ++st2) av[st2] = tr(st2 >> 4, st2 & 15);
-    bf16x8 p0 = soft8(ps, acc, 0, rem, scale_log2);
+    for (int s = 0; s < D; ++s) av[s] = tr(s >> 4, s & 15);
+    float p[16];
+    const bf16x8 p0 = soft8(acc, 0, ps.m_ref, scale_log2, p);
     bf16x8 p1;
 #pragma unroll
     for (int step = 0; step < 32; ++step) {
         const int kt = step >> 4, cb = step & 15;
         if (step + D < 32) av[(step + D) % (D + 1)] = tr((step + D) >> 4, (step + D) & 15);
         ps.o[cb] = mfma32(av[step % (D + 1)], kt == 0 ? p0 : p1, ps.o[cb]);
-        if (step == 3) p1 = soft8(ps, acc, 1, rem, scale_log2);
+        if (step == 2) p1 = soft8(acc, 1, ps.m_ref, scale_log2, p);
+        if (step == 8) {
+            float s0 = p[0], s1 = p[1];
+#pragma unroll
+            for (int i = 2; i < 16; i += 2) { s0 += p[i]; s1 += p[i + 1]; }
+            ps.lsum += s0 + s1;
+        }
+        if (step == 10) ps.mraw = max17_raw(ps.mraw, acc);
         __builtin_amdgcn_sched_barrier(0);
     }
+}
+
+// One tile: QK^T, the masking of rows past the split's end (last tile
+// only), the reference maximum (first tile of the first pass only), softmax
+// and PV.  hook(ks) issues the copies of a later tile between the QK^T
+// MFMAs.  All LDS reads of the tile go through the restrict pointers st
+// (this tile's stage) and smem_q (the Q~ blocks): the copies the hook issues
+// write another stage (the copy pipeline's own waits order them against
+// these reads), and the restrict scope tells the compiler so, which keeps it
+// from draining all copies before the first transposed PV read.
+template <typename Hook>
+__device__ __forceinline__ void compute_tile(const char* __restrict__ st, const char* __restrict__ smem_q,
+                                             const LaneOffsets& lo, const bf16x8 (&qreg)[QK_REG], PassState& ps,
+                                             float scale_log2, int rem, bool first, Hook&& hook) {
+    const int g = (threadIdx.x & 63) >> 5;
+    f32x16 acc;
+    qk_tile(st, smem_q, lo, qreg, acc, hook);
+    if (rem < R) {
+        // last tile, partly filled: rows past the end score -inf
+        const int rl = rem - 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if (8 * (i >> 2) + (i & 3) >= rl) acc[i] = -INFINITY;
+    }
+    if (first) {
+        // reference maximum: the first tile's, floored to an integer so
+        // that exp2(x - m_ref) differs from exp2(x) by a power of two only
+        // and its bf16 rounding does not depend on where the splits fall
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc[i]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+        ps.m_ref = floorf(mt);
+    }
+    pv_tile(st, lo, ps, acc, scale_log2);
 }
 
 // One pass over the split (see attn_kernel).  Returns true when the pass
@@ -324,9 +383,11 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ st, LaneOffsets
 //
 // Copy pipeline, per wave: iteration j fetches the indices of tile j+6 and
 // copies tile j+3 (9 copies, spread over the QK^T chain) into the stage tile
-// j-1 left; the prologue plays iterations -3..-1.  Iteration it waits until tile it has landed:
-// the copies issued after it (indices of it+4 and it+5, tiles it+1 and
-// it+2) may still be in flight.
+// j-1 left; the prologue plays iterations -3..-1.  Tiles past the split are
+// copied as well (from row 0 = "no row": zeros, no memory traffic), so
+// every iteration issues COPIES_PER_TILE copies and iteration it waits with
+// one constant count: the copies issued after tile it's (the index fetches
+// of tiles it+4, it+5 and the tiles it+1, it+2) may still be in flight.
 __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc, char* smem,
                                           float& m_ref, bool known) {
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -337,13 +398,18 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     if (tid == 0) *flag = 0;
 
     int* idx_ring = (int*)(smem + OFF_IDX) + wave * 8;      // + slot * 32
-    auto stage = [&](int T) { return smem + (T % NST) * STAGE; };
+    auto stage = [&](int T) { return (T % NST) * STAGE; };
+    MLA_LDS char* const lsm = (MLA_LDS char*)smem;
+    auto lstage = [&](int T) { return lsm + stage(T); };
     auto slot = [&](int T) { return idx_ring + (T % NSLOT) * 32; };
 
-    const LaneOffsets lo = lane_offsets();
+    const LaneOffsets lo = lane_offsets(a);
+    int mst[8];                                    // row_start of this wave's 8 rows
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mst[j] = __builtin_amdgcn_readfirstlane(row_start(wave * 8 + j));
     PassState ps;
     ps.m_ref = m_ref;
-    ps.m_true = known ? m_ref : -INFINITY;
+    ps.mraw = -INFINITY;
     ps.lsum = 0.f;
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) ps.o[cb] = f32x16{};
@@ -357,77 +423,56 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     // heads past H read as zero (outside the buffer window).
     const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
-    if (nt > 0) {
+    if (nt == 0) {
+        // empty split: no copies; the epilogue writes l = 0
+    } else {
 #pragma unroll
-        for (int T = 0; T < 3; ++T)
-            if (T < nt) fetch_idx(sc, T, slot(T));
+        for (int T = 0; T < 3; ++T) fetch_idx(sc, T, slot(T));
         wait_vmcnt<0>();
-    }
-    {
-        // LDS part: lane l fills bytes 16 l of the wave's 1 KB row of block i,
-        // i.e. head 32 wave + l/2, features 16 (QK_REG + i) + 8 (l & 1)
-        const uint32_t hq = (uint32_t)(sc.h0 + wave * 32 + (lane >> 1));
+        {
+            // LDS part: lane l fills bytes 16 l of the wave's 1 KB row of
+            // block i, i.e. head 32 wave + l/2, features 16 (QK_REG + i) + 8 (l & 1)
+            const uint32_t hq = (uint32_t)(sc.h0 + wave * 32 + (lane >> 1));
 #pragma unroll
-        for (int i = 0; i < QK_LDS; ++i)
-            buffer_to_lds16(qsrc, hq * (ROW * 2) + (16 * (QK_REG + i) + 8 * (lane & 1)) * 2,
-                            (MLA_LDS void*)(smem + OFF_Q + 4096 * i + 1024 * wave));
-    }
-    if (nt > 0) {
-        if (3 < nt) fetch_idx(sc, 3, slot(3));
-        issue_tile(a, sc, stage(0), slot(0));
-    }
-    {
-        const uint32_t h = (uint32_t)(sc.h0 + wave * 32 + l32);
+            for (int i = 0; i < QK_LDS; ++i)
+                buffer_to_lds16(qsrc, hq * (ROW * 2) + (16 * (QK_REG + i) + 8 * (lane & 1)) * 2,
+                                (MLA_LDS void*)(smem + OFF_Q + 4096 * i + 1024 * wave));
+        }
+        fetch_idx(sc, 3, slot(3));
+        issue_tile(a, sc, lo, mst, lstage(0), slot(0));
+        {
+            const uint32_t h = (uint32_t)(sc.h0 + wave * 32 + l32);
 #pragma unroll
-        for (int ks = 0; ks < QK_REG; ++ks)
-            qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
-    }
-    if (nt > 0) {
+            for (int ks = 0; ks < QK_REG; ++ks)
+                qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
+        }
 #pragma unroll
         for (int T = 1; T < 3; ++T) {
-            if (T + 3 < nt) fetch_idx(sc, T + 3, slot(T + 3));
-            if (T < nt) issue_tile(a, sc, stage(T), slot(T));
+            fetch_idx(sc, T + 3, slot(T + 3));
+            issue_tile(a, sc, lo, mst, lstage(T), slot(T));
         }
     }
 
     // ---- main loop ----
+    const int nrows = sc.end - sc.start;
     for (int it = 0; it < nt; ++it) {
-        // copies issued after tile it: indices of it+4 and it+5, tiles it+1
-        // and it+2, and (first iteration only) the Q~ register loads
-        wait_vm((it + 4 < nt) + 9 * (it + 1 < nt) + (it + 5 < nt) + 9 * (it + 2 < nt) + (it == 0 ? QK_REG : 0));
+        wait_vmcnt<2 * COPIES_PER_TILE>();
         lds_barrier();          // tile it resident and visible; stage (it-1)%4 free
-        const bool do_fetch = it + 6 < nt, do_issue = it + 3 < nt;
-        TileRows rows;
-        if (do_issue) rows = read_rows(slot(it + 3));
-        char* dst = stage(it + 3);
-        f32x16 acc;
-        qk_tile(stage(it), smem, lo, qreg, acc, [&](int ks) {
-            if (ks == 1 && do_fetch) fetch_idx(sc, it + 6, slot(it + 6));
-            if (do_issue) {
-                if (ks >= 2 && ks <= 30 && (ks - 2) % 4 == 0) issue_row(a, sc, dst, rows, (ks - 2) / 4);
-                if (ks == 34) issue_rot(a, sc, dst, rows);
-            }
+        const TileRows rows = read_rows(slot(it + 3));
+        const int st = stage(it);
+        MLA_LDS char* const dst = lstage(it + 3);
+        int* const fslot = slot(it + 6);
+        compute_tile(smem + st, smem, lo, qreg, ps, a.scale_log2, nrows - it * R, it == 0 && !known, [&](int ks) {
+            if (ks == 1) fetch_idx(sc, it + 6, fslot);
+            if (ks >= 2 && ks <= 30 && (ks - 2) % 4 == 0) issue_row(a, sc, lo, dst + mst[(ks - 2) / 4], rows, (ks - 2) / 4);
+            if (ks == 34) issue_rot(a, sc, lo, dst, rows);
         });
-        int g4 = 4 * g;
-        opaque(g4);
-        const int rem = sc.end - sc.start - it * R - g4;
-        if (it == 0 && !known) {
-            // reference maximum: the first tile's, floored to an integer so
-            // that exp2(x - m_ref) differs from exp2(x) by a power of two only
-            // and its bf16 rounding does not depend on where the splits fall
-            float mt = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                mt = fmaxf(mt, 8 * (i >> 2) + (i & 3) < rem ? acc[i] * a.scale_log2 : -INFINITY);
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
-            ps.m_ref = floorf(mt);
-        }
-        pv_tile(stage(it), lo, ps, acc, rem, a.scale_log2);
     }
 
     // ---- overflow check, then normalise and write ----
-    __syncthreads();
-    const float mx = fmaxf(ps.m_true, __shfl_xor(ps.m_true, 32));
+    __syncthreads();            // also drains the copies of the tiles past the split
+    const float mx = fmaxf(ps.mraw, __shfl_xor(ps.mraw, 32)) * a.scale_log2;
     if (!known && mx > ps.m_ref + P_EXP_LIMIT) *flag = 1;
     __syncthreads();
     if (!known && *flag) {
@@ -500,7 +545,7 @@ void attn_kernel(AttnArgs a) {
     sc.start = min(sc.s * rps, cnt);
     sc.end = min(sc.start + rps, cnt);
     sc.ntiles = (sc.end - sc.start + R - 1) / R;
-    sc.list = make_rsrc(a.list + (long long)sc.b * a.K, (uint32_t)a.K * 4u);
+    sc.list = make_rsrc(a.list + (long long)sc.b * a.K + sc.start, (uint32_t)(sc.end - sc.start) * 4u);
     sc.kv = make_rsrc(a.kv + (long long)sc.b * a.kv_sb, a.kv_win);
     sc.pe = make_rsrc(a.pe + (long long)sc.b * a.pe_sb, a.pe_win);
 

@@ -21,7 +21,7 @@ struct Plan {
 // Carve-up of the caller's workspace.
 struct Work {
     void* qt;           // Q~ [B][H][576] (bf16 or fp32)
-    int32_t* list;      // compacted selection [B][K]
+    int32_t* list;      // compacted selection [B][K], ascending, 1-based (position + 1)
     int32_t* counts;    // selected rows per sequence [B]
     uint32_t* status;   // validation status word
     void* opart;        // split partials [B][S][H][512] (bf16; fp32 path: [B][H][512] fp32)

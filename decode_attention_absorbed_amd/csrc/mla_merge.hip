@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
         const int j = base + tid;
         float sc = -INFINITY;
         if (j < cnt) {
-            const long long t = list[j];
+            const long long t = list[j] - 1;   // entries are 1-based
             const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
             const float* r = a.pe + b * a.pe_sb + t * a.pe_st;
             float acc = 0.f;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
         m = mn;
         const int nrow = min(256, cnt - base);
         for (int r = 0; r < nrow; ++r) {
-            const long long t = list[base + r];
+            const long long t = list[base + r] - 1;
             const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
             const float pr = ps[r];
             o0 = fmaf(pr, c[tid], o0);

@@ -228,7 +228,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
         uint32_t bits = bm[w];
         while (bits) {
             const int pos = (w << 5) + __ffs(bits) - 1;
-            out[off++] = pos;
+            out[off++] = pos + 1;                     // 1-based: 0 marks "no row"
             bits &= bits - 1;
         }
     }
