@@ -224,40 +224,6 @@ __device__ __forceinline__ void qk_settle(f32x16& acc) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(acc));
 }
 
-// QK^T of one tile for this wave's 32 heads: S^T[32 rows][32 heads] in acc
-// (lane l: head l%32, rows 8(i/4) + 4(l/32) + i%4 for i = 0..15); tile
-// operands are read QK_DEPTH steps ahead of the MFMAs.  hook(ks) runs after
-// the MFMA of step ks: the copies for a later tile are spread over the chain.
-template <typename Hook>
-__device__ __forceinline__ void qk_tile(const char* __restrict__ st, const char* __restrict__ smem_q,
-                                        const LaneOffsets& lo, const bf16x8 (&qreg)[QK_REG], f32x16& acc,
-                                        Hook&& hook) {
-    int base = lo.qk, rbase = lo.rot, qb = lo.q;
-    opaque(base);
-    opaque(rbase);
-    opaque(qb);
-    constexpr int NK = ROW / 16, D = QK_DEPTH;
-    bf16x8 kv[D + 1], qv[D + 1];
-    auto load = [&](int ks) {
-        const int addr = ks < 32 ? base + 32 * ks : (ks == 32 ? rbase : rbase ^ ((ks - 32) << 5));
-        kv[ks % (D + 1)] = *(const bf16x8*)(st + addr);
-        if (ks >= QK_REG) qv[ks % (D + 1)] = *(const bf16x8*)(smem_q + qb + 4096 * (ks - QK_REG));
-    };
-#pragma unroll
-    for (int ks = 0; ks < D; ++ks) load(ks);
-#pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-        if (ks + D < NK) load(ks + D);
-        const bf16x8 q = ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks % (D + 1)];
-        const bf16x8 k = kv[ks % (D + 1)];
-        if (ks == 0) qk_mfma_first(acc, k, q);
-        else qk_mfma(acc, k, q);
-        hook(ks);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    qk_settle(acc);
-}
-
 // max(m, x[0..15]) as eight v_max3_f32.  fmaxf on values the compiler
 // cannot prove canonical (results of the inline-asm MFMAs) costs an extra
 // NaN-quieting max per operand.
@@ -286,108 +252,158 @@ struct PassState {
     f32x16 o[16];       // [cb]: columns 32cb + 8(i/4) + 4(lane/32) + i%4 of head lane%32
 };
 
-// Probabilities of accumulator entries 8kt .. 8kt+7 (rows 16kt + 8(e/4) +
-// 4(lane/32) + e%4), exponentiated against the reference maximum (no clamp:
-// a probability that overflows means the split is recomputed, see
-// attn_pass); p keeps them in fp32 for the running sum, the return value is
-// the PV B operand of K step kt.
-__device__ __forceinline__ bf16x8 soft8(const f32x16& acc, int kt, float m_ref, float scale_log2, float (&p)[16]) {
-    bf16x8 pk;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int i = 8 * kt + e;
-        p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m_ref));
-        pk[e] = f2bf(p[i]);
-    }
-    return pk;
+// Probabilities of accumulator entries i and i+1, exponentiated against the
+// reference maximum and added to the running sum; packed into PV B operand
+// pk at e, e+1.  Called one pair per MFMA step so that the transcendental
+// unit never holds up an MFMA issue for long.
+__device__ __forceinline__ void soft2(const f32x16& acc, int i, float m_ref, float scale_log2, float& lsum,
+                                      bf16x8& pk, int e) {
+    const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m_ref));
+    const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i + 1], scale_log2, -m_ref));
+    lsum += pa + pb;
+    pk[e] = f2bf(pa);
+    pk[e + 1] = f2bf(pb);
 }
 
-// PV of one tile: O^T[cb] += V^T(kt, cb) . P^T(kt) for 16 column blocks and
-// two K steps of 16 rows.  The K index k = 8 (lane/32) + e of step kt is row
-// 16kt + 8(e/4) + 4(lane/32) + e%4, matching soft8's operand; the A operand
-// (columns x those rows) is two transposed reads of 4 rows each.  The second
-// K step's probabilities are computed while the first step's MFMAs run, the
-// running sum and maximum after them.
-__device__ __forceinline__ void pv_tile(const char* __restrict__ st, const LaneOffsets& lo,
-                                        PassState& ps, const f32x16& acc, float scale_log2) {
+// The tile loop's MFMA schedule.  Tile it is one run of 68 steps, one MFMA
+// each:
+//   steps  0.. 7  PV of tile it-1, K step 1 (its rows 16..31), column blocks 0..7
+//   steps  8..43  QK^T of tile it, feature blocks 0..35
+//   steps 44..51  PV of tile it-1, K step 1, column blocks 8..15
+//   steps 52..67  PV of tile it, K step 0 (rows 0..15), column blocks 0..15
+// so that no MFMA waits for the softmax: the probabilities of tile it's rows
+// 0..15 are computed during steps 44..51, which do not need them, and those
+// of rows 16..31 during steps 52..67 (they are used at the next tile's steps
+// 0..7).  The first QK^T operands are read during steps 0..7.  PV: O^T[cb]
+// += V^T(kt, cb) . P^T(kt); the K index k = 8 (lane/32) + e of step kt is
+// row 16kt + 8(e/4) + 4(lane/32) + e%4, matching soft8's operand, and the A
+// operand (columns x those rows) is two transposed reads of 4 rows each.
+// QK^T: S^T[32 rows][32 heads] in acc (lane l: head l%32, rows 8(i/4) +
+// 4(l/32) + i%4 for i = 0..15).
+// The A operand of step s is read AHEAD steps earlier into ring slot
+// s % RING (68 = 17 RING, so the slots line up from tile to tile); the
+// reads for the next tile's steps 0..2 (its PV of this tile, K step 1) are
+// issued during steps 65..67.
+constexpr int RING = 4;
+constexpr int AHEAD = RING - 1;
+constexpr int NSTEP = 68;
+static_assert(NSTEP % RING == 0, "ring alignment");
+
+// A operand of PV step (kt, cb) of the tile in stage st.
+__device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0, int t1, int kt, int cb) {
+    const int o = 1024 * kt + 64 * cb;
+    const bf16x4 r0 = lds_read_tr16((const MLA_LDS void*)(st + t0 + o));
+    const bf16x4 r1 = lds_read_tr16((const MLA_LDS void*)(st + t1 + o));
+    return cat(r0, r1);
+}
+
+// One tile (it) of the loop.  cur: its stage; prv: the previous tile's
+// stage.  All LDS reads go through the restrict pointers cur, prv (stages)
+// and smem_q (the Q~ blocks): the copies the hook issues write another stage
+// (the copy pipeline's own waits order them against these reads), and the
+// restrict scopes tell the compiler so, which keeps it from draining all
+// copies before the first transposed PV read.  hook(s) runs after the MFMA
+// of step s.
+template <typename Hook>
+__device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const char* __restrict__ prv,
+                                          const char* __restrict__ smem_q, const LaneOffsets& lo,
+                                          const bf16x8 (&qreg)[QK_REG], PassState& ps, bf16x8 (&ring)[RING],
+                                          bf16x8& ptail, float scale_log2, int rem, bool first, Hook&& hook) {
+    int qb = lo.qk, rb = lo.rot, t0 = lo.tr[0], t1 = lo.tr[1], qo = lo.q;
+    opaque(qb);
+    opaque(rb);
+    opaque(t0);
+    opaque(t1);
+    opaque(qo);
+    const int g = (threadIdx.x & 63) >> 5;
+    auto load = [&](int s) -> bf16x8 {
+        if (s >= NSTEP) return pv_operand(cur, t0, t1, 1, s - NSTEP);   // next tile's steps 0..
+        if (s < 8) return pv_operand(prv, t0, t1, 1, s);
+        if (s < 44) {
+            const int ks = s - 8;
+            const int addr = ks < 32 ? qb + 32 * ks : (ks == 32 ? rb : rb ^ ((ks - 32) << 5));
+            return *(const bf16x8*)(cur + addr);
+        }
+        if (s < 52) return pv_operand(prv, t0, t1, 1, 8 + s - 44);
+        return pv_operand(cur, t0, t1, 0, s - 52);
+    };
+    bf16x8 qv[QK_LDS];
+    f32x16 acc;
+    bf16x8 p0 = {}, p1 = {};
+#pragma clang loop unroll(full)
+    for (int s = 0; s < NSTEP; ++s) {
+        ring[(s + AHEAD) % RING] = load(s + AHEAD);
+        if (s + AHEAD >= 8 + QK_REG && s + AHEAD < 44)
+            qv[s + AHEAD - 8 - QK_REG] = *(const bf16x8*)(smem_q + qo + 4096 * (s + AHEAD - 8 - QK_REG));
+        const bf16x8 av = ring[s % RING];
+        if (s < 8 || (s >= 44 && s < 52)) {
+            const int cb = s < 8 ? s : 8 + s - 44;
+            ps.o[cb] = mfma32(av, ptail, ps.o[cb]);
+        } else if (s < 44) {
+            const int ks = s - 8;
+            const bf16x8 q = ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks >= QK_REG ? ks - QK_REG : 0];
+            if (ks == 0) qk_mfma_first(acc, av, q);
+            else qk_mfma(acc, av, q);
+        } else {
+            const int cb = s - 52;
+            ps.o[cb] = mfma32(av, p0, ps.o[cb]);
+        }
+        if (s == 43) {
+            qk_settle(acc);
+            if (rem < R) {
+                // last tile, partly filled: rows past the end score -inf
+                const int rl = rem - 4 * g;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (8 * (i >> 2) + (i & 3) >= rl) acc[i] = -INFINITY;
+            }
+            if (first) {
+                // reference maximum: the first tile's, floored to an integer
+                // so that exp2(x - m_ref) differs from exp2(x) by a power of
+                // two only and its bf16 rounding does not depend on where
+                // the splits fall
+                float mt = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc[i]);
+                mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
+                ps.m_ref = floorf(mt);
+            }
+        }
+        if (s >= 44 && s < 48) soft2(acc, 2 * (s - 44), ps.m_ref, scale_log2, ps.lsum, p0, 2 * (s - 44));
+        if (s == 49) ps.mraw = max17_raw(ps.mraw, acc);
+        if (s >= 53 && s < 57) soft2(acc, 8 + 2 * (s - 53), ps.m_ref, scale_log2, ps.lsum, p1, 2 * (s - 53));
+        hook(s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    ptail = p1;
+}
+
+// The last tile's K step 1 (steps 0..7 and 44..51 of a following tile that
+// does not exist).  Its first AHEAD operands are already in the ring.
+__device__ __forceinline__ void pv_last(const char* __restrict__ prv, const LaneOffsets& lo, PassState& ps,
+                                        bf16x8 (&ring)[RING], const bf16x8& ptail) {
     int t0 = lo.tr[0], t1 = lo.tr[1];
     opaque(t0);
     opaque(t1);
-    auto tr = [&](int kt, int cb) {
-        const int o = 1024 * kt + 64 * cb;
-        const bf16x4 r0 = lds_read_tr16((const MLA_LDS void*)(st + t0 + o));
-        const bf16x4 r1 = lds_read_tr16((const MLA_LDS void*)(st + t1 + o));
-        return cat(r0, r1);
-    };
-    constexpr int D = PV_DEPTH;
-    bf16x8 av[D + 1];
 #pragma unroll
-    for (int s = 0; s < D; ++s) av[s] = tr(s >> 4, s & 15);
-    float p[16];
-    const bf16x8 p0 = soft8(acc, 0, ps.m_ref, scale_log2, p);
-    bf16x8 p1;
-#pragma unroll
-    for (int step = 0; step < 32; ++step) {
-        const int kt = step >> 4, cb = step & 15;
-        if (step + D < 32) av[(step + D) % (D + 1)] = tr((step + D) >> 4, (step + D) & 15);
-        ps.o[cb] = mfma32(av[step % (D + 1)], kt == 0 ? p0 : p1, ps.o[cb]);
-        if (step == 2) p1 = soft8(acc, 1, ps.m_ref, scale_log2, p);
-        if (step == 8) {
-            float s0 = p[0], s1 = p[1];
-#pragma unroll
-            for (int i = 2; i < 16; i += 2) { s0 += p[i]; s1 += p[i + 1]; }
-            ps.lsum += s0 + s1;
-        }
-        if (step == 10) ps.mraw = max17_raw(ps.mraw, acc);
+    for (int cb = 0; cb < 16; ++cb) {
+        if (cb + AHEAD < 16) ring[(cb + AHEAD) % RING] = pv_operand(prv, t0, t1, 1, cb + AHEAD);
+        ps.o[cb] = mfma32(ring[cb % RING], ptail, ps.o[cb]);
         __builtin_amdgcn_sched_barrier(0);
     }
-}
-
-// One tile: QK^T, the masking of rows past the split's end (last tile
-// only), the reference maximum (first tile of the first pass only), softmax
-// and PV.  hook(ks) issues the copies of a later tile between the QK^T
-// MFMAs.  All LDS reads of the tile go through the restrict pointers st
-// (this tile's stage) and smem_q (the Q~ blocks): the copies the hook issues
-// write another stage (the copy pipeline's own waits order them against
-// these reads), and the restrict scope tells the compiler so, which keeps it
-// from draining all copies before the first transposed PV read.
-template <typename Hook>
-__device__ __forceinline__ void compute_tile(const char* __restrict__ st, const char* __restrict__ smem_q,
-                                             const LaneOffsets& lo, const bf16x8 (&qreg)[QK_REG], PassState& ps,
-                                             float scale_log2, int rem, bool first, Hook&& hook) {
-    const int g = (threadIdx.x & 63) >> 5;
-    f32x16 acc;
-    qk_tile(st, smem_q, lo, qreg, acc, hook);
-    if (rem < R) {
-        // last tile, partly filled: rows past the end score -inf
-        const int rl = rem - 4 * g;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            if (8 * (i >> 2) + (i & 3) >= rl) acc[i] = -INFINITY;
-    }
-    if (first) {
-        // reference maximum: the first tile's, floored to an integer so
-        // that exp2(x - m_ref) differs from exp2(x) by a power of two only
-        // and its bf16 rounding does not depend on where the splits fall
-        float mt = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, acc[i]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * scale_log2;
-        ps.m_ref = floorf(mt);
-    }
-    pv_tile(st, lo, ps, acc, scale_log2);
 }
 
 // One pass over the split (see attn_kernel).  Returns true when the pass
 // must be repeated with the exact maximum (then m_ref holds it).
 //
-// Copy pipeline, per wave: iteration j fetches the indices of tile j+6 and
-// copies tile j+3 (9 copies, spread over the QK^T chain) into the stage tile
-// j-1 left; the prologue plays iterations -3..-1.  Tiles past the split are
-// copied as well (from row 0 = "no row": zeros, no memory traffic), so
-// every iteration issues COPIES_PER_TILE copies and iteration it waits with
-// one constant count: the copies issued after tile it's (the index fetches
-// of tiles it+4, it+5 and the tiles it+1, it+2) may still be in flight.
+// Copy pipeline, per wave: iteration j fetches the indices of tile j+4 and
+// copies tile j+2 (9 copies, spread over the QK^T chain) into the stage that
+// tile j-2 left (its last reads were the previous iteration's PV, K step
+// 1); the prologue plays iterations -2..-1.  Tiles past the split are copied
+// as well (from row 0 = "no row": zeros, no memory traffic), so every
+// iteration issues COPIES_PER_TILE copies and iteration it waits with one
+// constant count: the copies issued after tile it's (the index fetch of
+// tile it+3 and tile it+1) may still be in flight.
 __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc, char* smem,
                                           float& m_ref, bool known) {
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -398,7 +414,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     if (tid == 0) *flag = 0;
 
     int* idx_ring = (int*)(smem + OFF_IDX) + wave * 8;      // + slot * 32
-    auto stage = [&](int T) { return (T % NST) * STAGE; };
+    auto stage = [&](int T) { return (T & (NST - 1)) * STAGE; };
     MLA_LDS char* const lsm = (MLA_LDS char*)smem;
     auto lstage = [&](int T) { return lsm + stage(T); };
     auto slot = [&](int T) { return idx_ring + (T % NSLOT) * 32; };
@@ -414,21 +430,23 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) ps.o[cb] = f32x16{};
 
+    // The first tile's steps 0..7 and 44..51 multiply the stage before stage
+    // 0 (stage NST-1) by zero probabilities: clear its latent region so that
+    // whatever it held cannot turn into NaN.
+    for (int i = tid; i < LATB / 16; i += 256) *(u32x4*)(smem + (NST - 1) * STAGE + 16 * i) = u32x4{};
+
     // ---- prologue ----
-    // Order of the copies (so that tile 0 does not wait behind Q~): indices
-    // of tiles 0..2; Q~ blocks 33..35 into LDS; indices of tile 3 and tile 0;
-    // Q~ blocks 0..32 into registers; indices 4 and tile 1; indices 5 and
-    // tile 2.  Q~ of this wave's 32 heads (QK^T B operand): block ks holds
-    // features 16 ks + 8 (lane/32) .. +7 of head h0 + 32 wave + lane%32;
-    // heads past H read as zero (outside the buffer window).
+    // Copy order: indices of tiles 0..1; Q~ (blocks 33..35 into LDS, blocks
+    // 0..32 into registers), which needs no index and is the largest
+    // transfer; then, once the indices have landed, indices 2 and tile 0,
+    // indices 3 and tile 1.  Q~ of this wave's 32 heads (QK^T B operand):
+    // block ks holds features 16 ks + 8 (lane/32) .. +7 of head h0 + 32 wave
+    // + lane%32; heads past H read as zero (outside the buffer window).
     const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
-    if (nt == 0) {
-        // empty split: no copies; the epilogue writes l = 0
-    } else {
+    if (nt > 0) {
 #pragma unroll
-        for (int T = 0; T < 3; ++T) fetch_idx(sc, T, slot(T));
-        wait_vmcnt<0>();
+        for (int T = 0; T < 2; ++T) fetch_idx(sc, T, slot(T));
         {
             // LDS part: lane l fills bytes 16 l of the wave's 1 KB row of
             // block i, i.e. head 32 wave + l/2, features 16 (QK_REG + i) + 8 (l & 1)
@@ -437,38 +455,47 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             for (int i = 0; i < QK_LDS; ++i)
                 buffer_to_lds16(qsrc, hq * (ROW * 2) + (16 * (QK_REG + i) + 8 * (lane & 1)) * 2,
                                 (MLA_LDS void*)(smem + OFF_Q + 4096 * i + 1024 * wave));
-        }
-        fetch_idx(sc, 3, slot(3));
-        issue_tile(a, sc, lo, mst, lstage(0), slot(0));
-        {
             const uint32_t h = (uint32_t)(sc.h0 + wave * 32 + l32);
 #pragma unroll
             for (int ks = 0; ks < QK_REG; ++ks)
                 qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                           qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
         }
+        wait_vmcnt<QK_LDS + QK_REG>();             // the two index fetches (issued first) landed
 #pragma unroll
-        for (int T = 1; T < 3; ++T) {
-            fetch_idx(sc, T + 3, slot(T + 3));
+        for (int T = 0; T < 2; ++T) {
+            fetch_idx(sc, T + 2, slot(T + 2));
             issue_tile(a, sc, lo, mst, lstage(T), slot(T));
         }
     }
 
     // ---- main loop ----
+    lds_barrier();                                 // the cleared stage visible
+    bf16x8 ring[RING];
+    bf16x8 ptail = {};
+    {
+        int t0 = lo.tr[0], t1 = lo.tr[1];
+        opaque(t0);
+        opaque(t1);
+#pragma unroll
+        for (int s = 0; s < AHEAD; ++s) ring[s] = pv_operand(smem + stage(NST - 1), t0, t1, 1, s);
+    }
     const int nrows = sc.end - sc.start;
     for (int it = 0; it < nt; ++it) {
-        wait_vmcnt<2 * COPIES_PER_TILE>();
-        lds_barrier();          // tile it resident and visible; stage (it-1)%4 free
-        const TileRows rows = read_rows(slot(it + 3));
-        const int st = stage(it);
-        MLA_LDS char* const dst = lstage(it + 3);
-        int* const fslot = slot(it + 6);
-        compute_tile(smem + st, smem, lo, qreg, ps, a.scale_log2, nrows - it * R, it == 0 && !known, [&](int ks) {
-            if (ks == 1) fetch_idx(sc, it + 6, fslot);
-            if (ks >= 2 && ks <= 30 && (ks - 2) % 4 == 0) issue_row(a, sc, lo, dst + mst[(ks - 2) / 4], rows, (ks - 2) / 4);
-            if (ks == 34) issue_rot(a, sc, lo, dst, rows);
+        wait_vmcnt<COPIES_PER_TILE>();
+        lds_barrier();          // tile it resident and visible; stage (it-2)%4 free
+        const TileRows rows = read_rows(slot(it + 2));
+        MLA_LDS char* const dst = lstage(it + 2);
+        int* const fslot = slot(it + 4);
+        tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, ps, ring, ptail, a.scale_log2,
+                  nrows - it * R, it == 0 && !known, [&](int st_) {
+            // copies of tile it+2 spread over the tile's 68 MFMA steps
+            if (st_ == 1) fetch_idx(sc, it + 4, fslot);
+            if (st_ >= 3 && st_ <= 59 && (st_ - 3) % 8 == 0) issue_row(a, sc, lo, dst + mst[(st_ - 3) / 8], rows, (st_ - 3) / 8);
+            if (st_ == 63) issue_rot(a, sc, lo, dst, rows);
         });
     }
+    if (nt > 0) pv_last(smem + stage(nt - 1), lo, ps, ring, ptail);
 
     // ---- overflow check, then normalise and write ----
     __syncthreads();            // also drains the copies of the tiles past the split

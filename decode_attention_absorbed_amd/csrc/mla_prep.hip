@@ -78,6 +78,9 @@ struct PrepArgs {
     uint32_t* status;
 };
 
+// Longest compacted list built in LDS (it overwrites the 64 KB bitmap area).
+constexpr int PREP_LIST_MAX = 16384;
+
 // Block-wide exclusive scan of one int per thread (256 threads).
 __device__ int block_exclusive_scan(int v, int* total, int* lds_wave) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -148,12 +151,14 @@ __device__ __forceinline__ void load_qpe32(const PrepArgs& a, int b, int h, int 
     }
 }
 
-// One sequence: the rotary query at p_b = L_b - 1 (pairs (2i, 2i+1) are one
-// complex number) and the selection compaction (every position listed in
-// the index row, minus -1 slots and entries outside [0, L_b), once,
-// ascending).  LDS holds a bitmap of ceil(L_b / 32) words.  The global
-// loads that do not depend on each other (cache length, the first 2048
-// indices, the first q_pe slices) are issued together up front.
+// One sequence: the selection compaction (every position listed in the
+// index row, minus -1 slots and entries outside [0, L_b), once, ascending)
+// and the rotary query at p_b = L_b - 1 (pairs (2i, 2i+1) are one complex
+// number).  LDS holds a bitmap of ceil(L_b / 32) words, then the compacted
+// list before it is copied out with coalesced stores.  The loads that do
+// not depend on each other (cache length, the first 2048 indices, the first
+// q_pe slices) are issued together; the rotation table row, which needs
+// L_b, is loaded while the selection runs.
 template <typename QtT, typename ActT>
 __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     __shared__ int lds_wave[4];
@@ -173,19 +178,16 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     float x[32];
     const bool rot0 = tid < 2 * a.H;                  // this thread's first (head, half)
     if (rot0) load_qpe32<ActT>(a, b, tid >> 1, 32 * (tid & 1), x);
-    // -- rotary query --
     const int p = min(max(L - 1, 0), a.Trope - 1);
     const float* cs = a.rope_table + (long long)p * D_ROPE;
-    for (int e = tid; e < a.H * 2; e += 256) {
-        const int h = e >> 1, f0 = 32 * (e & 1);
-        if (e != tid) load_qpe32<ActT>(a, b, h, f0, x);
-        float t[32];
+    float t[32];
+    if (rot0) {
+        const int f0 = 32 * (tid & 1);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const f32x4 v = *(const f32x4*)(cs + f0 + 4 * k);
             t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
         }
-        rotate32<QtT>(a, b, h, f0, x, t);
     }
     // -- selection --
     uint32_t status = 0;
@@ -224,17 +226,49 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
     int total;
     int off = block_exclusive_scan(cnt, &total, lds_wave);
     int32_t* out = a.list + (long long)b * a.K;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t bits = bm[w];
-        while (bits) {
-            const int pos = (w << 5) + __ffs(bits) - 1;
-            out[off++] = pos + 1;                     // 1-based: 0 marks "no row"
-            bits &= bits - 1;
+    if (total <= PREP_LIST_MAX && wpt <= 2) {
+        // each thread's (at most two) words into registers, then the list
+        // is built in LDS over the bitmap and copied out coalesced
+        uint32_t wd[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) wd[k] = w0 + k < w1 ? bm[w0 + k] : 0u;
+        __syncthreads();                              // every word read before the list overwrites them
+        int* ll = (int*)bm;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t bits = wd[k];
+            while (bits) {
+                ll[off++] = ((w0 + k) << 5) + __ffs(bits);   // 1-based: 0 marks "no row"
+                bits &= bits - 1;
+            }
+        }
+        __syncthreads();
+        for (int i = tid; i < total; i += 256) out[i] = ll[i];
+    } else {
+        for (int w = w0; w < w1; ++w) {
+            uint32_t bits = bm[w];
+            while (bits) {
+                out[off++] = (w << 5) + __ffs(bits);  // 1-based: 0 marks "no row"
+                bits &= bits - 1;
+            }
         }
     }
     if (tid == 0) {
         a.counts[b] = total;
         if (total == 0) status |= BAD_EMPTY;
+    }
+    // -- rotary query --
+    for (int e = tid; e < a.H * 2; e += 256) {
+        const int h = e >> 1, f0 = 32 * (e & 1);
+        if (e != tid) {
+            load_qpe32<ActT>(a, b, h, f0, x);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const f32x4 v = *(const f32x4*)(cs + f0 + 4 * k);
+                t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
+            }
+        }
+        rotate32<QtT>(a, b, h, f0, x, t);
     }
     if (status) atomicOr(&lds_status, status);
     __syncthreads();
@@ -247,9 +281,14 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // weight slice W_UK[h][0:128][64 columns] is read once with 16-byte loads,
 // converted to bf16 (fp32 weights split into a bf16 high part and a bf16
 // remainder, two MFMAs each, so they enter with ~16 significant bits) and
-// stored row-major in a wave-private LDS region; the MFMA operand (8
-// consecutive features of one column) is then read with ds_read_b64_tr_b16.
-constexpr int ABS_WAVE_LDS = D_NOPE * 64 * 2;         // one part: [128][64] bf16
+// passed through a wave-private LDS region, 64 feature rows at a time, to
+// be read back transposed (8 consecutive features of one column per lane,
+// ds_read_b64_tr_b16).  The queries q_nope[:, h, :] of up to 128 sequences
+// are copied into LDS once per block (buffer->LDS, issued together with the
+// weight loads) and shared by the 4 waves.
+constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // one staging round: [64 rows][64 columns] bf16
+constexpr int ABS_QROWS = 128;                        // sequences per query chunk
+constexpr int ABS_Q_OFF = 4 * ABS_WAVE_LDS;           // query chunk: [128][128] bf16, 256 B rows
 
 template <typename WT>
 __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
@@ -258,15 +297,33 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
     const WT* W = (const WT*)a.w_uk + h * a.wk_sh + c0;
-    char* wl = lds + wave * ABS_WAVE_LDS;             // row d, column c at d*128 + c*2 (swizzled)
-    // Row d holds 64 columns = 8 chunks of 16 bytes; chunk q sits at slot
-    // q ^ (d & 7) so that the transposed reads (4 rows x 16 columns per 16
-    // lanes) do not collide.
+    char* wl = lds + wave * ABS_WAVE_LDS;             // row d (0..63), column c at d*128 + c*2 (swizzled)
+    const char* ql = lds + ABS_Q_OFF;
+    // Staging row d holds 64 columns = 8 chunks of 16 bytes; chunk q sits at
+    // slot q ^ (d & 7) so that the transposed reads (4 rows x 16 columns per
+    // 16 lanes) do not collide.
     auto waddr = [&](int d, int c) {
         return d * 128 + ((((c >> 3) ^ (d & 7))) << 4) + (c & 7) * 2;
     };
+    // Query chunk in LDS: sequence row r (0..127) at r * 256, its 16-byte
+    // chunk k (features 8k..8k+7) at slot k ^ (r & 15): the MFMA operand read
+    // (32 rows at one chunk) then touches 16 distinct slots per 16 lanes.
+    // Copy: instruction i of a wave moves rows 4 (4 wave + i) + l/16, lane l
+    // filling slot l % 16, i.e. fetching chunk (l % 16) ^ (row & 15).
+    auto copy_q = [&](int b0) {
+        const int nrow = min(ABS_QROWS, a.B - b0);
+        const rsrc_t qs = make_rsrc((const bf16*)a.q_nope + b0 * a.qn_sb + h * a.qn_sh,
+                                    (uint32_t)((nrow - 1) * a.qn_sb * 2 + D_NOPE * 2));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int r = 4 * (8 * wave + i) + (lane >> 4);
+            const uint32_t off = (uint32_t)(r < nrow ? r * a.qn_sb * 2 : 0x7FFFFFFF) + (uint32_t)((((lane & 15) ^ (r & 15))) << 4);
+            buffer_to_lds16(qs, off, (MLA_LDS void*)(lds + ABS_Q_OFF + (8 * wave + i) * 1024));
+        }
+    };
     // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i,
-    // all 32 loads in flight at once.
+    // all 32 loads in flight at once, issued before the first query chunk's
+    // copies.
     const int cq = 4 * (lane & 15);
     float wv[D_NOPE / 4][4];
 #pragma unroll
@@ -282,6 +339,7 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
             for (int e = 0; e < 4; ++e) wv[i][e] = (float)x[e];
         }
     }
+    copy_q(0);
     // bf16 parts, packed right away so the fp32 values die early
     bf16x4 wp[NP][D_NOPE / 4];
 #pragma unroll
@@ -298,69 +356,67 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
     // 16 kb + 8 (blk >> 1) + 4 rr + j, columns 32 nb + 16 (blk & 1) + 4 q .. +3.
     const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
     bf16x8 bw[NP][2][8];
-    // The parts pass through the wave's LDS region one after the other:
-    // part 0 = bf16(w), part 1 = bf16(w - part 0).  A wave's LDS accesses run
-    // in order, so the second part's writes follow the first part's reads.
+    // The staging rounds (part pp, feature rows 64 hf .. 64 hf + 63) pass
+    // through the wave's LDS region one after the other.  A wave's LDS
+    // accesses run in order, so a round's writes follow the previous round's
+    // reads.
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp) {
+    for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-        for (int i = 0; i < D_NOPE / 4; ++i) *(bf16x4*)(wl + waddr((lane >> 4) + 4 * i, cq)) = wp[pp][i];
-        __builtin_amdgcn_s_waitcnt(0xC07F);           // this wave's writes done (only it reads them)
-        asm volatile("" ::: "memory");
+        for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+            for (int i = 0; i < 16; ++i) *(bf16x4*)(wl + waddr((lane >> 4) + 4 * i, cq)) = wp[pp][16 * hf + i];
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // this wave's writes done (only it reads them)
+            asm volatile("" ::: "memory");
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
-                bf16x4 r[2];
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int d = 16 * kb + 8 * (blk >> 1) + 4 * rr + jj;
-                    const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
-                    r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(d, c)));
+                for (int k4 = 0; k4 < 4; ++k4) {
+                    bf16x4 r[2];
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const int d = 16 * k4 + 8 * (blk >> 1) + 4 * rr + jj;
+                        const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
+                        r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(d, c)));
+                    }
+                    bw[pp][nb][4 * hf + k4] = cat(r[0], r[1]);
                 }
-                bw[pp][nb][kb] = cat(r[0], r[1]);
-            }
-        __builtin_amdgcn_s_waitcnt(0xC07F);           // reads done before the next part overwrites
-        asm volatile("" ::: "memory");
-    }
-
-    auto load_q = [&](int b0, bf16x8 (&aq)[8]) {
-        const int bA = b0 + l32;
-        if (bA < a.B) {
-            const bf16* q = (const bf16*)a.q_nope + bA * a.qn_sb + h * a.qn_sh;
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb) aq[kb] = *(const bf16x8*)(q + 16 * kb + 8 * g);
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 8; ++kb) aq[kb] = bf16x8{};
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // reads done before the next round overwrites
+            asm volatile("" ::: "memory");
         }
-    };
-    bf16x8 aqn[8];
-    load_q(0, aqn);
-    for (int b0 = 0; b0 < a.B; b0 += 32) {
-        const int bA = b0 + l32;
-        bf16x8 aq[8];
+
+    for (int b0 = 0; b0 < a.B; b0 += ABS_QROWS) {
+        if (b0 > 0) {
+            __syncthreads();                          // every wave done with the previous chunk
+            copy_q(b0);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();                              // the chunk's rows visible to every wave
+        const int nb0 = min(ABS_QROWS, a.B - b0);
+        for (int s0 = 0; s0 < nb0; s0 += 32) {
+            const int r = s0 + l32, bA = b0 + r;
+            bf16x8 aq[8];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) aq[kb] = aqn[kb];
-        if (b0 + 32 < a.B) load_q(b0 + 32, aqn);     // next sequences' queries in flight
-        // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
-        // sequence b0 + l%32 and columns 8(i/4) + 4(l/32) + i%4, so each lane
-        // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
+            for (int kb = 0; kb < 8; ++kb) aq[kb] = *(const bf16x8*)(ql + r * 256 + (((2 * kb + g) ^ (r & 15)) << 4));
+            // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l
+            // holds sequence bA and columns 8(i/4) + 4(l/32) + i%4, so each lane
+            // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-            f32x16 acc = {};
+            for (int nb = 0; nb < 2; ++nb) {
+                f32x16 acc = {};
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+                for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-                for (int pp = 0; pp < NP; ++pp) acc = mfma32(bw[pp][nb][kb], aq[kb], acc);
-            if (bA < a.B) {
-                bf16* dst = (bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 32 * nb + 4 * g;
+                    for (int pp = 0; pp < NP; ++pp) acc = mfma32(bw[pp][nb][kb], aq[kb], acc);
+                if (bA < a.B) {
+                    bf16* dst = (bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 32 * nb + 4 * g;
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    bf16x4 v;
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        bf16x4 v;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) v[r] = f2bf(acc[4 * i4 + r]);
-                    *(bf16x4*)(dst + 8 * i4) = v;
+                        for (int rr = 0; rr < 4; ++rr) v[rr] = f2bf(acc[4 * i4 + rr]);
+                        *(bf16x4*)(dst + 8 * i4) = v;
+                    }
                 }
             }
         }
@@ -390,7 +446,7 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
 // LDS of a prep block: the absorption's weight staging (4 waves) or the
 // selection bitmap of up to 2^19 positions.  64 KB lets two blocks share a
 // CU, so selection blocks run beside absorption blocks.
-constexpr int PREP_LDS = 4 * ABS_WAVE_LDS;
+constexpr int PREP_LDS = ABS_Q_OFF + ABS_QROWS * D_NOPE * 2;
 static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 
 // Blocks [0, B) prepare one sequence each (selection, rotary query); blocks
