@@ -60,6 +60,7 @@ bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_split
         S = base >= num_cus ? 1 : num_cus / base;
         const int max_by_rows = (K + 2 * pl->tile_rows - 1) / (2 * pl->tile_rows);
         if (S > max_by_rows) S = max_by_rows;
+        if ((int64_t)S * H > 65536) S = 65536 / H;   // keeps 32 sequences' partials within 2 GiB
         if (S < 1) S = 1;
     }
     if (S > kMaxSplits) return false;
@@ -185,12 +186,25 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream) {
     if ((int64_t)(p->max_cache_len - 1) * p->kv_stride_t * 2 + 1024 > INT32_MAX ||
         (int64_t)(p->max_cache_len - 1) * p->pe_stride_t * 2 + 128 > INT32_MAX)
         return fail(MLA_ERR_UNSUPPORTED, "one sequence's cache rows span more than 2 GiB");
+    // the absorption copies 128 sequences' queries at a time with 32-bit byte offsets
+    if ((int64_t)127 * p->q_nope_stride_b * 2 + 256 > INT32_MAX)
+        return fail(MLA_ERR_UNSUPPORTED, "q_nope batch stride too large");
 
     int num_cus = p->num_cus;
     if (num_cus == 0 && query_num_cus(&num_cus) != 0) return fail(MLA_ERR_HIP, "cannot query the device");
     mla::Plan plan;
     if (!make_plan(p->B, p->H, p->K, p->dtype_act, num_cus, p->num_splits, &plan))
         return fail(MLA_ERR_INVALID_ARG, "no launch plan (fp32 activations take num_splits 0 or 1)");
+    if (plan.bf16_path) {
+        // the merge kernel addresses the output, the split partials (32
+        // sequences at a time) and the split LSEs with 32-bit byte offsets
+        const int64_t osz = p->dtype_out == MLA_DTYPE_F32 ? 4 : 2;
+        const int64_t out_ext = ((int64_t)(p->B - 1) * p->out_stride_b + (int64_t)(p->H - 1) * p->out_stride_h + 128) * osz;
+        const int64_t part_ext = 31 * (int64_t)plan.splits * p->H * 1024 + 1024;
+        const int64_t lse_ext = (int64_t)p->B * plan.splits * p->H * 4;
+        if (out_ext > INT32_MAX || part_ext > INT32_MAX || lse_ext > INT32_MAX)
+            return fail(MLA_ERR_UNSUPPORTED, "output or split partials exceed the 2 GiB offset range");
+    }
     mla::Work w;
     const size_t need = mla::workspace_layout(p->B, p->H, p->K, plan.bf16_path, plan.splits, p->workspace, &w);
     if (p->workspace_size < need)

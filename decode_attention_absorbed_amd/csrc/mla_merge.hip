@@ -44,6 +44,29 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
     if (h >= a.H) return;
     const int col0 = (RANK / MW) * wave;
 
+    // The partials are consumed in units of (32 sequences, 2 splits); unit
+    // u + 1 is loaded while unit u is processed, across the reduction of a
+    // finished batch too, so the memory system never idles between batches.
+    // Splits are combined with a running maximum (rescaling what was summed
+    // when the maximum grows).
+    const int G = (a.S + 1) / 2;                     // split pairs per sequence
+    const int U = ((a.B + 31) / 32) * G;
+    auto load_unit = [&](int u, bf16x8 (&v)[2][MKB], float (&ls)[2]) {
+        const int bA = 32 * (u / G) + l32, s0 = 2 * (u % G);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int s = s0 + t;
+            const bool ok = bA < a.B && s < a.S;
+            const long long row = ((long long)bA * a.S + s) * a.H + h;
+            ls[t] = ok ? a.lsepart[row] : -INFINITY;
+            const bf16* src = a.opart + row * RANK + col0 + 8 * g;
+#pragma unroll
+            for (int kb = 0; kb < MKB; ++kb) v[t][kb] = ok ? *(const bf16x8*)(src + 16 * kb) : bf16x8{};
+        }
+    };
+    bf16x8 vc[2][MKB], vn[2][MKB];
+    float lc[2], ln[2];
+    load_unit(0, vc, lc);           // first partials in flight together with the weights
     // fp32 weights enter as bf16 hi + lo parts (two MFMAs each).
     constexpr int NP = sizeof(WT) == 4 ? 2 : 1;
     const WT* W = (const WT*)a.w_uv + h * a.wv_sh;
@@ -69,29 +92,6 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
         }
     }
 
-    // The partials are consumed in units of (32 sequences, 2 splits); unit
-    // u + 1 is loaded while unit u is processed, across the reduction of a
-    // finished batch too, so the memory system never idles between batches.
-    // Splits are combined with a running maximum (rescaling what was summed
-    // when the maximum grows).
-    const int G = (a.S + 1) / 2;                     // split pairs per sequence
-    const int U = ((a.B + 31) / 32) * G;
-    auto load_unit = [&](int u, bf16x8 (&v)[2][MKB], float (&ls)[2]) {
-        const int bA = 32 * (u / G) + l32, s0 = 2 * (u % G);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int s = s0 + t;
-            const bool ok = bA < a.B && s < a.S;
-            const long long row = ((long long)bA * a.S + s) * a.H + h;
-            ls[t] = ok ? a.lsepart[row] : -INFINITY;
-            const bf16* src = a.opart + row * RANK + col0 + 8 * g;
-#pragma unroll
-            for (int kb = 0; kb < MKB; ++kb) v[t][kb] = ok ? *(const bf16x8*)(src + 16 * kb) : bf16x8{};
-        }
-    };
-    bf16x8 vc[2][MKB], vn[2][MKB];
-    float lc[2], ln[2];
-    load_unit(0, vc, lc);
     float M = -INFINITY, Wsum = 0.f;
     float xs[MKB][8];
 #pragma unroll
