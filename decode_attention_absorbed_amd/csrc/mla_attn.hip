@@ -280,14 +280,18 @@ __device__ __forceinline__ void soft2(const f32x16& acc, int i, float m_ref, flo
 // operand (columns x those rows) is two transposed reads of 4 rows each.
 // QK^T: S^T[32 rows][32 heads] in acc (lane l: head l%32, rows 8(i/4) +
 // 4(l/32) + i%4 for i = 0..15).
-// The A operand of step s is read AHEAD steps earlier into ring slot
-// s % RING (68 = 17 RING, so the slots line up from tile to tile); the
-// reads for the next tile's steps 0..2 (its PV of this tile, K step 1) are
-// issued during steps 65..67.
+// PV operands: PV step p (0..31 in a tile: p = s for s < 8, s - 36 for s
+// >= 44) is read PV_AHEAD PV steps earlier into ring slot p % RING (32 =
+// 8 RING, so the slots line up from tile to tile); the reads for the next
+// tile's PV steps 0..2 (its PV of this tile, K step 1) are issued during
+// steps 65..67.  QK^T operands: feature block ks is read QK_AHEAD steps
+// earlier into slot ks % (QK_AHEAD + 1) of a ring that lives within the
+// tile (its first reads are issued during steps 3..7).
 constexpr int RING = 4;
-constexpr int AHEAD = RING - 1;
+constexpr int PV_AHEAD = RING - 1;
+constexpr int QK_AHEAD = 5;
 constexpr int NSTEP = 68;
-static_assert(NSTEP % RING == 0, "ring alignment");
+static_assert(32 % RING == 0, "ring alignment");
 
 // A operand of PV step (kt, cb) of the tile in stage st.
 __device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0, int t1, int kt, int cb) {
@@ -316,37 +320,39 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
     opaque(t1);
     opaque(qo);
     const int g = (threadIdx.x & 63) >> 5;
-    auto load = [&](int s) -> bf16x8 {
-        if (s >= NSTEP) return pv_operand(cur, t0, t1, 1, s - NSTEP);   // next tile's steps 0..
-        if (s < 8) return pv_operand(prv, t0, t1, 1, s);
-        if (s < 44) {
-            const int ks = s - 8;
-            const int addr = ks < 32 ? qb + 32 * ks : (ks == 32 ? rb : rb ^ ((ks - 32) << 5));
-            return *(const bf16x8*)(cur + addr);
-        }
-        if (s < 52) return pv_operand(prv, t0, t1, 1, 8 + s - 44);
-        return pv_operand(cur, t0, t1, 0, s - 52);
+    auto pv_load = [&](int p) -> bf16x8 {
+        if (p >= 32) return pv_operand(cur, t0, t1, 1, p - 32);        // next tile's tail
+        if (p < 16) return pv_operand(prv, t0, t1, 1, p);               // tail: previous tile, K step 1
+        return pv_operand(cur, t0, t1, 0, p - 16);                      // head: this tile, K step 0
     };
+    auto qk_load = [&](int ks) -> bf16x8 {
+        const int addr = ks < 32 ? qb + 32 * ks : (ks == 32 ? rb : rb ^ ((ks - 32) << 5));
+        return *(const bf16x8*)(cur + addr);
+    };
+    bf16x8 kv[QK_AHEAD + 1];
     bf16x8 qv[QK_LDS];
     f32x16 acc;
     bf16x8 p0 = {}, p1 = {};
 #pragma clang loop unroll(full)
     for (int s = 0; s < NSTEP; ++s) {
-        ring[(s + AHEAD) % RING] = load(s + AHEAD);
-        if (s + AHEAD >= 8 + QK_REG && s + AHEAD < 44)
-            qv[s + AHEAD - 8 - QK_REG] = *(const bf16x8*)(smem_q + qo + 4096 * (s + AHEAD - 8 - QK_REG));
-        const bf16x8 av = ring[s % RING];
-        if (s < 8 || (s >= 44 && s < 52)) {
-            const int cb = s < 8 ? s : 8 + s - 44;
-            ps.o[cb] = mfma32(av, ptail, ps.o[cb]);
-        } else if (s < 44) {
+        const bool is_qk = s >= 8 && s < 44;
+        const int pvs = s < 8 ? s : s - 36;                             // PV step index (PV steps only)
+        if (!is_qk) ring[(pvs + PV_AHEAD) % RING] = pv_load(pvs + PV_AHEAD);
+        if (s >= 8 - QK_AHEAD && s < 44 - QK_AHEAD) {
+            const int kl = s - (8 - QK_AHEAD);
+            kv[kl % (QK_AHEAD + 1)] = qk_load(kl);
+            if (kl >= QK_REG) qv[kl - QK_REG] = *(const bf16x8*)(smem_q + qo + 4096 * (kl - QK_REG));
+        }
+        if (!is_qk) {
+            const bf16x8 av = ring[pvs % RING];
+            const int cb = pvs & 15;
+            ps.o[cb] = mfma32(av, pvs < 16 ? ptail : p0, ps.o[cb]);
+        } else {
             const int ks = s - 8;
             const bf16x8 q = ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks >= QK_REG ? ks - QK_REG : 0];
-            if (ks == 0) qk_mfma_first(acc, av, q);
-            else qk_mfma(acc, av, q);
-        } else {
-            const int cb = s - 52;
-            ps.o[cb] = mfma32(av, p0, ps.o[cb]);
+            const bf16x8 k = kv[ks % (QK_AHEAD + 1)];
+            if (ks == 0) qk_mfma_first(acc, k, q);
+            else qk_mfma(acc, k, q);
         }
         if (s == 43) {
             qk_settle(acc);
@@ -379,7 +385,7 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
 }
 
 // The last tile's K step 1 (steps 0..7 and 44..51 of a following tile that
-// does not exist).  Its first AHEAD operands are already in the ring.
+// does not exist).  Its first PV_AHEAD operands are already in the ring.
 __device__ __forceinline__ void pv_last(const char* __restrict__ prv, const LaneOffsets& lo, PassState& ps,
                                         bf16x8 (&ring)[RING], const bf16x8& ptail) {
     int t0 = lo.tr[0], t1 = lo.tr[1];
@@ -387,7 +393,7 @@ __device__ __forceinline__ void pv_last(const char* __restrict__ prv, const Lane
     opaque(t1);
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) {
-        if (cb + AHEAD < 16) ring[(cb + AHEAD) % RING] = pv_operand(prv, t0, t1, 1, cb + AHEAD);
+        if (cb + PV_AHEAD < 16) ring[(cb + PV_AHEAD) % RING] = pv_operand(prv, t0, t1, 1, cb + PV_AHEAD);
         ps.o[cb] = mfma32(ring[cb % RING], ptail, ps.o[cb]);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -478,7 +484,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
         opaque(t0);
         opaque(t1);
 #pragma unroll
-        for (int s = 0; s < AHEAD; ++s) ring[s] = pv_operand(smem + stage(NST - 1), t0, t1, 1, s);
+        for (int s = 0; s < PV_AHEAD; ++s) ring[s] = pv_operand(smem + stage(NST - 1), t0, t1, 1, s);
     }
     const int nrows = sc.end - sc.start;
     for (int it = 0; it < nt; ++it) {
