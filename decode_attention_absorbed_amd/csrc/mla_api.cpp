@@ -98,6 +98,21 @@ extern "C" {
 
 const char* mla_last_error(void) { return g_err; }
 
+int mla_topk(const mla_topk_params_t* p, void* stream) {
+    g_err[0] = 0;
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "mla_topk: null params");
+    if (!p->scores || !p->cache_lens || !p->topk_indices)
+        return fail(MLA_ERR_INVALID_ARG, "mla_topk: null pointer");
+    if (p->B < 1 || p->B > kMaxBatch || p->k < 1 || p->max_len < 1 || p->max_len > kMaxCacheLen || p->reserved != 0)
+        return fail(MLA_ERR_INVALID_ARG, "mla_topk: sizes out of range (B=%d k=%d max_len=%d)", p->B, p->k, p->max_len);
+    if (p->score_stride < p->max_len || p->idx_stride < p->k)
+        return fail(MLA_ERR_INVALID_ARG, "mla_topk: a stride is smaller than its row");
+    if (mla::launch_topk(p->B, p->k, p->max_len, p->scores, p->score_stride, p->cache_lens, p->topk_indices,
+                         p->idx_stride, (hipStream_t)stream) != hipSuccess)
+        return fail(MLA_ERR_HIP, "mla_topk: launch failed");
+    return MLA_OK;
+}
+
 size_t mla_decode_params_size(void) { return sizeof(mla_decode_params_t); }
 
 double mla_softmax_scale(int qk_head_dim, const mla_rope_cfg_t* cfg) {

@@ -37,5 +37,7 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
                        hipStream_t s);
 hipError_t launch_attn(const mla_decode_params_t& p, const Plan& plan, const Work& w, hipStream_t s);
 hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Work& w, hipStream_t s);
+hipError_t launch_topk(int B, int k, int max_len, const float* scores, long long score_stride,
+                       const int32_t* cache_lens, int32_t* out, long long out_stride, hipStream_t s);
 
 }  // namespace mla

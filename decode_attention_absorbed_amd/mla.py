@@ -57,6 +57,14 @@ class DecodeParams(ctypes.Structure):
                 ("validate_status", ctypes.c_uint32), ("reserved0", ctypes.c_uint32)]
 
 
+class TopkParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("k", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("reserved", ctypes.c_int32),
+                ("scores", _P), ("score_stride", _I64),
+                ("cache_lens", _P),
+                ("topk_indices", _P), ("idx_stride", _I64)]
+
+
 _lib = None
 
 
@@ -79,6 +87,8 @@ def lib():
         L.mla_decode_attn.restype = ctypes.c_int
         L.mla_decode_params_size.argtypes = []
         L.mla_decode_params_size.restype = ctypes.c_size_t
+        L.mla_topk.argtypes = [ctypes.POINTER(TopkParams), _P]
+        L.mla_topk.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
         L.mla_last_error.restype = ctypes.c_char_p
         if L.mla_decode_params_size() != ctypes.sizeof(DecodeParams):
@@ -232,3 +242,24 @@ def decode(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_len
                      softmax_scale, out, lse, workspace, num_splits=num_splits, validate=validate)
     decode_attn(p, stream)
     return out, lse
+
+
+def topk(scores, cache_lens, k, out=None, stream=None):
+    """mla_topk: int32 [B, k] ascending positions of the min(k, L_b) largest
+    scores per row (-1 padded).  scores: float32 [B, L] (inner dim contiguous),
+    cache_lens: int32 [B]; all on the device."""
+    torch = _torch()
+    B, L = scores.shape
+    if scores.dtype != torch.float32 or scores.stride(1) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, "scores must be float32 with a contiguous inner dimension")
+    if out is None:
+        out = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    p = TopkParams()
+    p.B, p.k, p.max_len, p.reserved = B, k, L, 0
+    p.scores, p.score_stride = scores.data_ptr(), scores.stride(0)
+    p.cache_lens = cache_lens.data_ptr()
+    p.topk_indices, p.idx_stride = out.data_ptr(), out.stride(0)
+    rc = lib().mla_topk(ctypes.byref(p), _stream_handle(stream))
+    if rc != MLA_OK:
+        raise MLAError(rc, last_error())
+    return out

@@ -213,6 +213,35 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream);
  * can check its own struct layout before the first call. */
 size_t mla_decode_params_size(void);
 
+/* ---- top-k selection ---------------------------------------------------- */
+typedef struct mla_topk_params {
+    int32_t B;                 /* sequences, 1..2^20 */
+    int32_t k;                 /* selection size and output row width, >= 1 */
+    int32_t max_len;           /* positions per scores row, 1..2^19 */
+    int32_t reserved;          /* must be 0 */
+    /* scores [B][score_stride] float32 on the device, score_stride >= max_len */
+    const float* scores;       int64_t score_stride;
+    /* cache_lens [B] int32 on the device: L_b, clamped to [0, max_len] */
+    const int32_t* cache_lens;
+    /* topk_indices [B][idx_stride] int32 on the device (output), idx_stride >= k */
+    int32_t* topk_indices;     int64_t idx_stride;
+} mla_topk_params_t;
+
+/*
+ * mla_topk -- the indexer's selection step, which produces the index rows
+ * mla_decode_attn consumes [page "Rotated query part", excerpt mla-decode:
+ * topk_indices = indexer(...), then the index mask; the indexer's scoring
+ * is not on the pages].  For every sequence b: the positions of the
+ * k_b = min(k, L_b) largest of scores[b][0 .. L_b), written ascending to
+ * topk_indices[b][0 .. k_b), then -1 up to k.  Scores compare in IEEE
+ * order with -0 equal to +0 and NaN below every other value; among scores
+ * equal to the k_b-th largest, the lowest positions are taken.
+ * Enqueues one kernel on `stream`.  Returns MLA_OK, MLA_ERR_INVALID_ARG
+ * (null pointer, sizes or strides out of range, reserved != 0) or
+ * MLA_ERR_HIP (launch failure).
+ */
+int mla_topk(const mla_topk_params_t* p, void* stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* mla_last_error(void);
 

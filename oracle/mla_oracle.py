@@ -180,6 +180,28 @@ def selection_mask(indices_row, L_b: int) -> np.ndarray:
     return mask
 
 
+def topk_select(scores_row, L_b: int, k: int) -> np.ndarray:
+    """The indexer's selection step (NEXT row f1): positions of the
+    min(k, L_b) largest of scores_row[0:L_b], ascending.  [mla-decode]:
+    ``topk_indices = self.indexer(...)`` supplies the positions the index
+    mask opens; the indexer's scoring is not on the pages, only that its
+    output is a set of positions in [0, L_b).  Reading (the pages leave the
+    order of equal scores open): scores compare as real numbers (-0 == +0),
+    NaN ranks below every other value, and among equal scores the lower
+    position ranks higher.  Written as a plain sort over (rank key, position)."""
+    L_b = max(0, int(L_b))
+    s = np.asarray(scores_row, dtype=np.float64).reshape(-1)[:L_b]
+
+    def rank_key(p):
+        v = s[p]
+        if v != v:                                   # NaN: lowest class
+            return (0, 0.0, -p)
+        return (1, float(v) + 0.0, -p)               # + 0.0 folds -0 into +0
+
+    order = sorted(range(L_b), key=rank_key, reverse=True)
+    return np.array(sorted(order[:min(k, L_b)]), dtype=np.int64)
+
+
 # ---------------------------------------------------------------------------
 # The decode step, non-absorbed definition (a3..a11 as one definition)
 # ---------------------------------------------------------------------------

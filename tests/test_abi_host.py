@@ -122,3 +122,25 @@ def test_rope_freqs_host_checks(mla):
     assert mla.lib().mla_rope_freqs(ctypes.byref(cfg), None, None) == mla.MLA_ERR_INVALID_ARG
     cfg = mla.rope_cfg(dict(W.ROPE_YARN, theta=0.5))
     assert mla.lib().mla_rope_freqs(ctypes.byref(cfg), ctypes.c_void_p(1 << 20), None) == mla.MLA_ERR_INVALID_ARG
+
+
+def _topk_params(mla, **kw):
+    p = mla.TopkParams()
+    p.B, p.k, p.max_len, p.reserved = 4, 64, 1000, 0
+    p.scores, p.score_stride = 1 << 20, 1000
+    p.cache_lens = 1 << 21
+    p.topk_indices, p.idx_stride = 1 << 22, 64
+    for name, v in kw.items():
+        setattr(p, name, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value", [
+    ("B", 0), ("k", 0), ("max_len", 0), ("max_len", (1 << 19) + 1), ("reserved", 1),
+    ("scores", 0), ("cache_lens", 0), ("topk_indices", 0), ("score_stride", 999), ("idx_stride", 63),
+])
+def test_topk_host_checks(mla, field, value):
+    p = _topk_params(mla, **{field: value})
+    assert mla.lib().mla_topk(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
+    assert "mla_topk" in mla.last_error()
+    assert mla.lib().mla_topk(None, None) == mla.MLA_ERR_INVALID_ARG

@@ -1,0 +1,109 @@
+"""Parity of mla_topk (the top-k selection step) with the oracle's topk_select.
+
+Index output is compared bit-exactly: both sides use the same order (NaN
+lowest, -0 == +0, ties to the lower position), so the selected set, its
+ascending order and the -1 padding are unique.
+"""
+import numpy as np
+import pytest
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from decode_attention_absorbed_amd import mla  # noqa: E402
+
+
+def _expected(scores, lens, k):
+    B = scores.shape[0]
+    out = np.full((B, k), -1, dtype=np.int64)
+    for b in range(B):
+        sel = oracle.topk_select(scores[b], int(lens[b]), k)
+        out[b, :sel.size] = sel
+    return out
+
+
+def _run(scores, lens, k):
+    s = torch.from_numpy(np.ascontiguousarray(scores, dtype=np.float32)).cuda()
+    l = torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda()
+    got = mla.topk(s, l, k)
+    torch.cuda.synchronize()
+    return got.cpu().numpy().astype(np.int64)
+
+
+def _check(scores, lens, k, name):
+    got = _run(scores, lens, k)
+    want = _expected(scores.astype(np.float32).astype(np.float64), lens, k)
+    bad = np.nonzero((got != want).any(axis=1))[0]
+    print(f"[topk {name}] B={scores.shape[0]} L={scores.shape[1]} k={k}: {bad.size} rows differ", flush=True)
+    assert bad.size == 0, f"rows {bad[:5]} differ: got {got[bad[0]][:10]} want {want[bad[0]][:10]}"
+
+
+def test_topk_random_ragged():
+    rng = np.random.default_rng(1101)
+    B, L, k = 12, 5000, 300
+    scores = rng.standard_normal((B, L)).astype(np.float32)
+    lens = np.array([0, 1, 299, 300, 301, 5000, 4096, 1234, 2, 3000, 4999, 777])
+    _check(scores, lens, k, "random ragged")
+
+
+def test_topk_ties_nan_signed_zero():
+    rng = np.random.default_rng(1102)
+    B, L, k = 8, 3000, 257
+    scores = rng.integers(-3, 4, size=(B, L)).astype(np.float32)   # heavy ties at the threshold
+    scores[rng.random((B, L)) < 0.05] = np.nan
+    scores[rng.random((B, L)) < 0.1] = -0.0
+    scores[rng.random((B, L)) < 0.02] = -np.inf
+    scores[rng.random((B, L)) < 0.01] = np.inf
+    lens = rng.integers(200, L + 1, size=B)
+    _check(scores, lens, k, "ties")
+
+
+def test_topk_all_equal_and_k_one():
+    B, L = 3, 1000
+    scores = np.zeros((B, L), dtype=np.float32)
+    _check(scores, np.array([1000, 10, 500]), 64, "all equal")
+    rng = np.random.default_rng(1103)
+    _check(rng.standard_normal((B, L)).astype(np.float32), np.array([1000, 1, 999]), 1, "k=1")
+
+
+def test_topk_rows_beyond_lds():
+    # rows longer than the 32768 keys kept in LDS re-read the scores each pass
+    rng = np.random.default_rng(1104)
+    B, L, k = 2, 70000, 2048
+    scores = rng.standard_normal((B, L)).astype(np.float32)
+    _check(scores, np.array([70000, 40000]), k, "long rows")
+
+
+def test_topk_decode_shape_sampled():
+    # the long-context decode shape: 64 rows of 16384 scores, k = 2048
+    rng = np.random.default_rng(1105)
+    B, L, k = 64, 16384, 2048
+    scores = rng.standard_normal((B, L)).astype(np.float32)
+    lens = np.full(B, L)
+    got = _run(scores, lens, k)
+    for b in (0, 17, 63):
+        want = oracle.topk_select(scores[b].astype(np.float64), L, k)
+        assert np.array_equal(got[b], want), b
+
+
+def test_topk_feeds_decode():
+    # mla_topk's rows used as the decode step's selection give the oracle's
+    # output for the oracle's selection
+    import workloads as W
+    from gpu_util import Dev, oracle_ref, rel_l2_rows
+    w = W.build("topk_feed", 2, 128, [700, 1500], 512, "bf16", "bf16", W.ROPE_YARN, seed=1106)
+    rng = np.random.default_rng(1107)
+    scores = rng.standard_normal((2, w.L_max)).astype(np.float32)
+    sel = _run(scores, w.cache_lens, 512)
+    w.topk_indices = sel.astype(np.int32)
+    dev = Dev(w)
+    out, lse, _ = dev.run()
+    ref, _ = oracle_ref(w)
+    err = rel_l2_rows(out.float().cpu().numpy(), ref).max()
+    print(f"[topk feed] max rel L2 {err:.3e}", flush=True)
+    assert err <= 1e-2

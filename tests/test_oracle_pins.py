@@ -333,3 +333,66 @@ def test_max_rel_l2():
     ref = np.array([[3.0, 4.0], [1.0, 0.0]])
     got = np.array([[3.0, 4.5], [1.0, 0.001]])
     assert oracle.max_rel_l2(got, ref) == pytest.approx(0.1)
+
+
+# ---------------------------------------------------------------------------
+# NEXT row f1: top-k selection.  The oracle sorts; the pins below use a
+# different, order-free definition (a position is selected iff fewer than
+# k_b positions outrank it) and hand-worked cases.
+# ---------------------------------------------------------------------------
+def _outranks(s, q, p):
+    """Does position q rank above position p?  NaN lowest, -0 == +0, ties to the lower position."""
+    a, b = s[q], s[p]
+    a_nan, b_nan = a != a, b != b
+    if a_nan or b_nan:
+        if a_nan and b_nan:
+            return q < p
+        return b_nan
+    if a != b:
+        return a > b
+    return q < p
+
+
+def _topk_by_rank_count(s, L_b, k):
+    L_b = max(0, L_b)
+    kb = min(k, L_b)
+    return [p for p in range(L_b) if sum(_outranks(s, q, p) for q in range(L_b) if q != p) < kb]
+
+
+def test_topk_hand_cases():
+    s = [0.5, 3.0, -1.0, 3.0, 2.0, float("nan"), 0.0]
+    assert list(oracle.topk_select(s, 7, 2)) == [1, 3]
+    assert list(oracle.topk_select(s, 7, 3)) == [1, 3, 4]
+    # the tie at the threshold goes to the lower position
+    assert list(oracle.topk_select([1.0, 2.0, 2.0, 2.0], 4, 2)) == [1, 2]
+    # -0 equals +0: the tie keeps the lower position
+    assert list(oracle.topk_select([-0.0, 0.0, -5.0], 3, 1)) == [0]
+    # NaN ranks below -inf
+    assert list(oracle.topk_select([float("nan"), -np.inf], 2, 1)) == [1]
+    # only positions below L_b count; k >= L_b selects them all
+    assert list(oracle.topk_select([1.0, 9.0, 9.0, 9.0], 2, 1)) == [1]
+    assert list(oracle.topk_select([1.0, 2.0, 3.0], 3, 5)) == [0, 1, 2]
+    assert list(oracle.topk_select([1.0], 0, 3)) == []
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_equals_rank_count_definition(seed):
+    rng = np.random.default_rng(900 + seed)
+    for _ in range(20):
+        L = int(rng.integers(1, 24))
+        k = int(rng.integers(1, 26))
+        L_b = int(rng.integers(0, L + 1))
+        s = rng.integers(-3, 4, size=L).astype(np.float64)      # many ties
+        s[rng.random(L) < 0.1] = np.nan
+        s[rng.random(L) < 0.1] = -0.0
+        s[rng.random(L) < 0.05] = -np.inf
+        assert list(oracle.topk_select(s, L_b, k)) == _topk_by_rank_count(s, L_b, k)
+
+
+def test_topk_invariants_on_continuous_scores():
+    rng = np.random.default_rng(77)
+    s = rng.standard_normal(5000)
+    sel = oracle.topk_select(s, 4000, 300)
+    assert sel.size == 300 and np.all(np.diff(sel) > 0) and sel.max() < 4000
+    rest = np.setdiff1d(np.arange(4000), sel)
+    assert s[sel].min() > s[rest].max()
