@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmla_decode.so")
-SOURCES = ["mla_api.cpp", "mla_prep.hip", "mla_attn.hip", "mla_merge.hip", "mla_topk.hip"]
+SOURCES = ["mla_api.cpp", "mla_prep.hip", "mla_attn.hip", "mla_merge.hip", "mla_topk.hip", "mla_rope.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

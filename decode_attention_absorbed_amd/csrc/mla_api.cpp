@@ -27,6 +27,8 @@ constexpr int kMaxCacheLen = 1 << 19;
 constexpr int kMaxBatch = 1 << 20;
 constexpr int kMaxHeads = 1 << 12;
 constexpr int kMaxSplits = 64;
+constexpr int kMaxRopeRows = 1 << 24;
+constexpr long long kMaxRopeVectors = 1ll << 27;   // 8 threads each: the grid stays below 2^31
 
 int query_num_cus(int* out) {
     int dev = 0;
@@ -110,6 +112,41 @@ int mla_topk(const mla_topk_params_t* p, void* stream) {
     if (mla::launch_topk(p->B, p->k, p->max_len, p->scores, p->score_stride, p->cache_lens, p->topk_indices,
                          p->idx_stride, (hipStream_t)stream) != hipSuccess)
         return fail(MLA_ERR_HIP, "mla_topk: launch failed");
+    return MLA_OK;
+}
+
+int mla_rope_apply(const mla_rope_apply_params_t* p, void* stream) {
+    g_err[0] = 0;
+    if (!p) return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: null params");
+    if (!p->x || !p->y || !p->positions || !p->rope_table)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: null pointer");
+    if (p->N < 1 || p->N > kMaxRopeRows || p->H < 1 || p->H > kMaxHeads || p->table_len < 1 || p->reserved != 0)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: sizes out of range (N=%d H=%d table_len=%d)", p->N, p->H,
+                    p->table_len);
+    if (p->dtype != MLA_DTYPE_BF16 && p->dtype != MLA_DTYPE_F32)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: dtype must be MLA_DTYPE_BF16 or MLA_DTYPE_F32");
+    if (p->interleaved != 0 && p->interleaved != 1)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: interleaved must be 0 or 1");
+    if ((long long)p->N * p->H > kMaxRopeVectors)
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: N*H exceeds %lld", kMaxRopeVectors);
+    // 64 features per vector; the vectors of one row must not overlap
+    auto strides_ok = [&](long long sn, long long sh) {
+        if (sh < 64 || sn < 0 || sn % 8 != 0 || sh % 8 != 0) return false;
+        if (p->N > 1 && sn < (long long)(p->H - 1) * sh + 64) return false;
+        return true;
+    };
+    if (!strides_ok(p->x_stride_n, p->x_stride_h) || !strides_ok(p->y_stride_n, p->y_stride_h))
+        return fail(MLA_ERR_INVALID_ARG,
+                    "mla_rope_apply: strides must be multiples of 8 with stride_h >= 64 and stride_n >= "
+                    "(H-1)*stride_h + 64");
+    if (!aligned16(p->x) || !aligned16(p->y) || !aligned16(p->rope_table))
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: x, y and rope_table must be 16-byte aligned");
+    if (p->x == p->y && (p->x_stride_n != p->y_stride_n || p->x_stride_h != p->y_stride_h))
+        return fail(MLA_ERR_INVALID_ARG, "mla_rope_apply: in place (x == y) needs equal strides");
+    if (mla::launch_rope_apply(p->N, p->H, p->dtype == MLA_DTYPE_BF16, p->interleaved == 1, p->table_len, p->x,
+                               p->x_stride_n, p->x_stride_h, p->y, p->y_stride_n, p->y_stride_h, p->positions,
+                               p->rope_table, (hipStream_t)stream) != hipSuccess)
+        return fail(MLA_ERR_HIP, "mla_rope_apply: launch failed");
     return MLA_OK;
 }
 

@@ -39,5 +39,9 @@ hipError_t launch_attn(const mla_decode_params_t& p, const Plan& plan, const Wor
 hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Work& w, hipStream_t s);
 hipError_t launch_topk(int B, int k, int max_len, const float* scores, long long score_stride,
                        const int32_t* cache_lens, int32_t* out, long long out_stride, hipStream_t s);
+hipError_t launch_rope_apply(int N, int H, bool bf16_io, bool interleaved, int table_len,
+                             const void* x, long long xs_n, long long xs_h,
+                             void* y, long long ys_n, long long ys_h,
+                             const int32_t* positions, const float* table, hipStream_t s);
 
 }  // namespace mla

@@ -65,6 +65,14 @@ class TopkParams(ctypes.Structure):
                 ("topk_indices", _P), ("idx_stride", _I64)]
 
 
+class RopeApplyParams(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int32), ("H", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("interleaved", ctypes.c_int32), ("table_len", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("x", _P), ("x_stride_n", _I64), ("x_stride_h", _I64),
+                ("y", _P), ("y_stride_n", _I64), ("y_stride_h", _I64),
+                ("positions", _P), ("rope_table", _P)]
+
+
 _lib = None
 
 
@@ -89,6 +97,8 @@ def lib():
         L.mla_decode_params_size.restype = ctypes.c_size_t
         L.mla_topk.argtypes = [ctypes.POINTER(TopkParams), _P]
         L.mla_topk.restype = ctypes.c_int
+        L.mla_rope_apply.argtypes = [ctypes.POINTER(RopeApplyParams), _P]
+        L.mla_rope_apply.restype = ctypes.c_int
         L.mla_last_error.argtypes = []
         L.mla_last_error.restype = ctypes.c_char_p
         if L.mla_decode_params_size() != ctypes.sizeof(DecodeParams):
@@ -260,6 +270,39 @@ def topk(scores, cache_lens, k, out=None, stream=None):
     p.cache_lens = cache_lens.data_ptr()
     p.topk_indices, p.idx_stride = out.data_ptr(), out.stride(0)
     rc = lib().mla_topk(ctypes.byref(p), _stream_handle(stream))
+    if rc != MLA_OK:
+        raise MLAError(rc, last_error())
+    return out
+
+
+def rope_apply(x, positions, rope_table, interleaved, out=None, stream=None):
+    """mla_rope_apply: rotate every 64-wide vector of x ([N, 64] or [N, H, 64],
+    bf16 or float32, last dim contiguous) at positions[n] (int32 [N]) with the
+    table from rope_freqs.  interleaved=True pairs (2i, 2i+1), False pairs
+    (i, i+32).  out may be x itself (in place); by default a new tensor."""
+    torch = _torch()
+    squeeze = x.dim() == 2
+    xv = x.unsqueeze(1) if squeeze else x
+    if xv.dim() != 3 or xv.shape[2] != 64 or xv.stride(2) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, "x must be [N, 64] or [N, H, 64] with a contiguous last dim")
+    if x.dtype == torch.bfloat16:
+        dt = MLA_DTYPE_BF16
+    elif x.dtype == torch.float32:
+        dt = MLA_DTYPE_F32
+    else:
+        raise MLAError(MLA_ERR_INVALID_ARG, "x must be bfloat16 or float32")
+    if out is None:
+        out = torch.empty_like(x, memory_format=torch.contiguous_format)
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise MLAError(MLA_ERR_INVALID_ARG, "out must match x in shape and dtype")
+    yv = out.unsqueeze(1) if squeeze else out
+    p = RopeApplyParams()
+    p.N, p.H = xv.shape[0], xv.shape[1]
+    p.dtype, p.interleaved, p.table_len, p.reserved = dt, 1 if interleaved else 0, rope_table.shape[0], 0
+    p.x, p.x_stride_n, p.x_stride_h = xv.data_ptr(), xv.stride(0), xv.stride(1)
+    p.y, p.y_stride_n, p.y_stride_h = yv.data_ptr(), yv.stride(0), yv.stride(1)
+    p.positions, p.rope_table = positions.data_ptr(), rope_table.data_ptr()
+    rc = lib().mla_rope_apply(ctypes.byref(p), _stream_handle(stream))
     if rc != MLA_OK:
         raise MLAError(rc, last_error())
     return out

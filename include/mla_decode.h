@@ -242,6 +242,44 @@ typedef struct mla_topk_params {
  */
 int mla_topk(const mla_topk_params_t* p, void* stream);
 
+/* ---- rotary embedding at per-row positions ------------------------------ */
+typedef struct mla_rope_apply_params {
+    int32_t N;                 /* rows (tokens or sequences), 1..2^24 */
+    int32_t H;                 /* 64-wide vectors per row (heads), 1..4096; N*H <= 2^27 */
+    int32_t dtype;             /* MLA_DTYPE_BF16 or MLA_DTYPE_F32, for x and y */
+    int32_t interleaved;       /* 1: pairs (2i, 2i+1); 0: pairs (i, i+32) */
+    int32_t table_len;         /* rows of rope_table */
+    int32_t reserved;          /* must be 0 */
+    /* x [N][H][64] on the device, element strides: row x_stride_n, vector
+     * x_stride_h; both multiples of 8, x_stride_h >= 64 and
+     * x_stride_n >= (H-1)*x_stride_h + 64; 16-byte aligned base */
+    const void* x;             int64_t x_stride_n;  int64_t x_stride_h;
+    /* y: same shape and rules (output); y == x with equal strides rotates in
+     * place; any other overlap of x and y is undefined */
+    void* y;                   int64_t y_stride_n;  int64_t y_stride_h;
+    /* positions [N] int32 on the device: t_n for every vector of row n */
+    const int32_t* positions;
+    /* rope_table from mla_rope_freqs(): [table_len][32][2] float32, 16-byte aligned */
+    const float* rope_table;
+} mla_rope_apply_params_t;
+
+/*
+ * mla_rope_apply -- rotary embedding of every 64-wide vector x[n][h] at
+ * position t_n [page "Rotated query part", excerpt apply-rope; table from
+ * page "Transformer blocks / RoPE coefficients"]: the 32 feature pairs are
+ * complex numbers z_i multiplied by cos(t theta'_i) + i sin(t theta'_i)
+ * = rope_table[t][i].  interleaved = 1 pairs features (2i, 2i+1), the layout
+ * of the attention path's rotary query and key; interleaved = 0 pairs
+ * (i, i+32), the indexer's layout (the vector viewed as [2][32] and
+ * transposed; real parts written to 0..31, imaginary parts to 32..63).
+ * fp32 arithmetic; bf16 output rounds to nearest even.  A position outside
+ * [0, table_len) is a precondition violation: that row's vectors are
+ * written as NaN.  Enqueues one kernel on `stream`.  Returns MLA_OK,
+ * MLA_ERR_INVALID_ARG (null pointer, sizes, strides or alignment out of
+ * range, reserved != 0) or MLA_ERR_HIP (launch failure).
+ */
+int mla_rope_apply(const mla_rope_apply_params_t* p, void* stream);
+
 /* Text of the last error on the calling thread ("" if none). */
 const char* mla_last_error(void);
 

@@ -150,6 +150,21 @@ def rope_rotate(x: np.ndarray, position: int, cfg: RopeConfig) -> np.ndarray:
     return y
 
 
+def rope_rotate_halves(x: np.ndarray, position: int, cfg: RopeConfig) -> np.ndarray:
+    """Rotate the last axis at one position in the non-interleaved layout
+    (NEXT row f2; the indexer's layout).  [apply-rope] with interleaved=False:
+    the features are viewed as [2, d/2] and transposed, so pair i is
+    (x[i], x[i + d/2]); after the complex multiplication the real parts come
+    first, then the imaginary parts."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    pairs = np.swapaxes(x.reshape(*x.shape[:-1], 2, d // 2), -1, -2)   # [..., d/2, 2]
+    z = pairs[..., 0] + 1j * pairs[..., 1]
+    cs = rope_cos_sin([position], cfg)[0]
+    z = z * (cs[:, 0] + 1j * cs[:, 1])
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
 # ---------------------------------------------------------------------------
 # a5: selection
 # ---------------------------------------------------------------------------

@@ -144,3 +144,36 @@ def test_topk_host_checks(mla, field, value):
     assert mla.lib().mla_topk(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
     assert "mla_topk" in mla.last_error()
     assert mla.lib().mla_topk(None, None) == mla.MLA_ERR_INVALID_ARG
+
+
+def _rope_params(mla, **kw):
+    p = mla.RopeApplyParams()
+    p.N, p.H, p.dtype, p.interleaved, p.table_len, p.reserved = 8, 4, mla.MLA_DTYPE_BF16, 0, 4096, 0
+    p.x, p.x_stride_n, p.x_stride_h = 1 << 20, 256, 64
+    p.y, p.y_stride_n, p.y_stride_h = 1 << 22, 256, 64
+    p.positions, p.rope_table = 1 << 23, 1 << 24
+    for name, v in kw.items():
+        setattr(p, name, v)
+    return p
+
+
+@pytest.mark.parametrize("field,value", [
+    ("N", 0), ("H", 0), ("H", 4097), ("table_len", 0), ("reserved", 1), ("dtype", 2), ("interleaved", 2),
+    ("x", 0), ("y", 0), ("positions", 0), ("rope_table", 0),
+    ("x_stride_h", 60), ("x_stride_h", 68), ("x_stride_n", 248), ("y_stride_n", 200), ("y_stride_h", 4),
+    ("x", (1 << 20) + 8), ("rope_table", (1 << 24) + 4),
+])
+def test_rope_apply_host_checks(mla, field, value):
+    p = _rope_params(mla, **{field: value})
+    assert mla.lib().mla_rope_apply(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
+    assert "mla_rope_apply" in mla.last_error()
+
+
+def test_rope_apply_host_checks_size_and_alias(mla):
+    # N*H above 2^27 vectors
+    p = _rope_params(mla, N=1 << 24, H=16, x_stride_n=1024, y_stride_n=1024)
+    assert mla.lib().mla_rope_apply(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
+    # in place with different strides
+    p = _rope_params(mla, y=1 << 20, y_stride_n=512)
+    assert mla.lib().mla_rope_apply(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
+    assert mla.lib().mla_rope_apply(None, None) == mla.MLA_ERR_INVALID_ARG

@@ -396,3 +396,44 @@ def test_topk_invariants_on_continuous_scores():
     assert sel.size == 300 and np.all(np.diff(sel) > 0) and sel.max() < 4000
     rest = np.setdiff1d(np.arange(4000), sel)
     assert s[sel].min() > s[rest].max()
+
+
+# ---------------------------------------------------------------------------
+# NEXT row f2: the non-interleaved (half-split) rotary layout
+# ---------------------------------------------------------------------------
+def test_rope_halves_is_interleaved_under_the_pair_permutation():
+    # pair i is (x[i], x[i+32]) in the half-split layout and (x[2i], x[2i+1])
+    # interleaved: permuting the input into interleaved order, rotating, and
+    # permuting back gives the same vector
+    rng = np.random.default_rng(55)
+    x = rng.standard_normal(64)
+    perm = np.empty(64, dtype=int)
+    perm[0::2] = np.arange(32)
+    perm[1::2] = np.arange(32) + 32
+    for p in (0, 1, 17, 4095, 16383):
+        y_int = oracle.rope_rotate(x[perm], p, YARN)
+        y = np.empty(64)
+        y[:32] = y_int[0::2]
+        y[32:] = y_int[1::2]
+        assert np.allclose(oracle.rope_rotate_halves(x, p, YARN), y, rtol=0, atol=1e-13)
+
+
+def test_rope_halves_pair0_worked_value(closed_forms):
+    # pair 0 = (x[0], x[32]) rotated by t * theta'_0 = t (theta'_0 = 1)
+    x = np.zeros(64)
+    x[0], x[32] = 1.0, 0.0
+    y = oracle.rope_rotate_halves(x, 1, YARN)
+    assert abs(y[0] - math.cos(1.0)) < 1e-15 and abs(y[32] - math.sin(1.0)) < 1e-15
+    x[0], x[32] = 0.0, 1.0
+    y = oracle.rope_rotate_halves(x, 1, YARN)
+    assert abs(y[0] + math.sin(1.0)) < 1e-15 and abs(y[32] - math.cos(1.0)) < 1e-15
+
+
+def test_rope_halves_identity_norm_relative_position():
+    rng = np.random.default_rng(56)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    assert np.allclose(oracle.rope_rotate_halves(q, 0, YARN), q, atol=1e-15)
+    assert abs(np.linalg.norm(oracle.rope_rotate_halves(q, 999, YARN)) - np.linalg.norm(q)) < 1e-12
+    d1 = oracle.rope_rotate_halves(q, 700, YARN) @ oracle.rope_rotate_halves(k, 500, YARN)
+    d2 = oracle.rope_rotate_halves(q, 1200, YARN) @ oracle.rope_rotate_halves(k, 1000, YARN)
+    assert abs(d1 - d2) < 1e-10
