@@ -42,6 +42,8 @@ Readings where the pages are silent (each is listed in the design doc):
   * Angles are exact (fp64); the page computes them in fp32.
   * The query of sequence b sits at position p_b = L_b - 1 (L = P + 1 keys).
   * The rope-key cache already holds keys rotated at their own positions.
+  * A fused append writes the new token's latent unchanged and its rotary
+    key rotated at p_b (interleaved) into row p_b (cache_append).
   * Selection is a set shared by all heads; -1 marks an unused slot;
     duplicates count once; an index outside [0, L_b) or an empty set is an
     error.
@@ -163,6 +165,30 @@ def rope_rotate_halves(x: np.ndarray, position: int, cfg: RopeConfig) -> np.ndar
     cs = rope_cos_sin([position], cfg)[0]
     z = z * (cs[:, 0] + 1j * cs[:, 1])
     return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def cache_append(kv_cache, pe_cache, kv_new, pe_new, cache_lens, cfg: RopeConfig):
+    """The new token's row written into the caches before it is attended to
+    (NEXT row f3).  [mla-init]: the joint down-projection emits the latent
+    (RMS-normalised before caching; that step stays outside, kv_new is the
+    normalised latent) and one rotary key shared by all heads.  The write
+    itself is not on the pages; the reading taken: for each sequence b the
+    row p_b = L_b - 1 (the new token's own position, [attn-weights]) gets
+    C[b, p_b] = kv_new[b] and R[b, p_b] = the rotary key rotated at p_b with
+    the same table and interleaved layout as the query ([apply-rope]), so a
+    query-key dot product depends on the positions only through their
+    difference.  Returns new fp64 arrays; the inputs are not modified."""
+    C = _f64(kv_cache).copy()
+    R = _f64(pe_cache).copy()
+    kv_new = _f64(kv_new)
+    pe_new = _f64(pe_new)
+    for b, L in enumerate(np.asarray(cache_lens).reshape(-1)):
+        L = int(L)
+        if L < 1 or L > C.shape[1]:
+            raise ValueError(f"sequence {b}: cache length {L} outside [1, {C.shape[1]}]")
+        C[b, L - 1] = kv_new[b]
+        R[b, L - 1] = rope_rotate(pe_new[b], L - 1, cfg)
+    return C, R
 
 
 # ---------------------------------------------------------------------------

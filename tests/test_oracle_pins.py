@@ -437,3 +437,67 @@ def test_rope_halves_identity_norm_relative_position():
     d1 = oracle.rope_rotate_halves(q, 700, YARN) @ oracle.rope_rotate_halves(k, 500, YARN)
     d2 = oracle.rope_rotate_halves(q, 1200, YARN) @ oracle.rope_rotate_halves(k, 1000, YARN)
     assert abs(d1 - d2) < 1e-10
+
+
+# ---------------------------------------------------------------------------
+# NEXT row f3: the fused cache append
+# ---------------------------------------------------------------------------
+def test_cache_append_writes_only_row_p_b():
+    rng = np.random.default_rng(57)
+    B, Lmax = 3, 9
+    C = rng.standard_normal((B, Lmax, 512))
+    R = rng.standard_normal((B, Lmax, 64))
+    kv_new = rng.standard_normal((B, 512))
+    pe_new = rng.standard_normal((B, 64))
+    lens = np.array([1, 9, 4])
+    C2, R2 = oracle.cache_append(C, R, kv_new, pe_new, lens, YARN)
+    for b, L in enumerate(lens):
+        other = [t for t in range(Lmax) if t != L - 1]
+        assert np.array_equal(C2[b, other], C[b, other]) and np.array_equal(R2[b, other], R[b, other])
+        assert np.array_equal(C2[b, L - 1], kv_new[b])              # latent copied, not transformed
+    # position 0 rotates by nothing
+    assert np.allclose(R2[0, 0], pe_new[0], rtol=0, atol=1e-15)
+    # the inputs are left alone
+    assert not np.array_equal(C[1, 8], kv_new[1])
+    with pytest.raises(ValueError):
+        oracle.cache_append(C, R, kv_new, pe_new, np.array([0, 1, 1]), YARN)
+
+
+def test_cache_append_key_matches_query_at_zero_offset():
+    # a query rotated at p_b and the appended key (rotated at its own p_b)
+    # have the dot product of the raw vectors, at any p_b; a key rotated at
+    # another position, in the other layout or not at all would not
+    rng = np.random.default_rng(58)
+    B, Lmax = 4, 16384
+    lens = np.array([2, 4097, 9000, 16384])
+    C = np.zeros((B, Lmax, 512))
+    R = np.zeros((B, Lmax, 64))
+    kv_new = rng.standard_normal((B, 512))
+    pe_new = rng.standard_normal((B, 64))
+    _, R2 = oracle.cache_append(C, R, kv_new, pe_new, lens, YARN)
+    for b, L in enumerate(lens):
+        q = rng.standard_normal(64)
+        got = oracle.rope_rotate(q, int(L) - 1, YARN) @ R2[b, L - 1]
+        assert abs(got - q @ pe_new[b]) < 1e-11
+        assert abs(oracle.rope_rotate(q, int(L) - 1, YARN) @ pe_new[b] - q @ pe_new[b]) > 1e-3
+
+
+def test_cache_append_then_single_row_decode_is_w_uv_times_new_latent():
+    # selecting only the new row after the append gives out[h] = W_UV[h] kv_new
+    rng = np.random.default_rng(59)
+    B, H, Lmax = 2, 3, 12
+    C = rng.standard_normal((B, Lmax, 512))
+    R = rng.standard_normal((B, Lmax, 64))
+    kv_new = rng.standard_normal((B, 512))
+    pe_new = rng.standard_normal((B, 64))
+    lens = np.array([5, 12])
+    C2, R2 = oracle.cache_append(C, R, kv_new, pe_new, lens, YARN)
+    idx = np.array([[4, -1], [11, -1]], dtype=np.int32)
+    q_nope = rng.standard_normal((B, H, 128))
+    q_pe = rng.standard_normal((B, H, 64))
+    w_uk = rng.standard_normal((H, 128, 512)) * 0.05
+    w_uv = rng.standard_normal((H, 128, 512)) * 0.05
+    out, _ = oracle.decode_attention(q_nope, q_pe, w_uk, w_uv, C2, R2, idx, lens, YARN)
+    for b in range(B):
+        for h in range(H):
+            assert np.allclose(out[b, h], w_uv[h] @ kv_new[b], rtol=1e-12, atol=1e-12)
