@@ -222,6 +222,16 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream) {
         if (!aligned16(ptrs[i])) return fail(MLA_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[i]);
     }
     if (p->lse_out && ((uintptr_t)p->lse_out & 3u)) return fail(MLA_ERR_INVALID_ARG, "lse_out misaligned");
+    if ((p->kv_new == nullptr) != (p->pe_new == nullptr))
+        return fail(MLA_ERR_INVALID_ARG, "kv_new and pe_new must both be set (fused append) or both be null");
+    if (p->kv_new) {
+        if (!aligned16(p->kv_new) || !aligned16(p->pe_new))
+            return fail(MLA_ERR_INVALID_ARG, "kv_new and pe_new must be 16-byte aligned");
+        if (p->kv_new_stride_b < 0 || (p->kv_new_stride_b & 7) || p->pe_new_stride_b < 0 || (p->pe_new_stride_b & 7))
+            return fail(MLA_ERR_INVALID_ARG, "kv_new/pe_new strides must be non-negative multiples of 8");
+        if (p->B > 1 && (p->kv_new_stride_b < 512 || p->pe_new_stride_b < 64))
+            return fail(MLA_ERR_INVALID_ARG, "kv_new/pe_new batch stride smaller than its row");
+    }
     const int64_t vec_strides[] = {p->q_nope_stride_b, p->q_nope_stride_h, p->q_pe_stride_b, p->q_pe_stride_h,
                                    p->w_uk_stride_h, p->w_uv_stride_h, p->kv_stride_b, p->kv_stride_t,
                                    p->pe_stride_b, p->pe_stride_t};

@@ -72,11 +72,69 @@ struct PrepArgs {
     const int32_t* idx; long long idx_sb;
     const int32_t* cache_lens;
     const float* rope_table;
+    // fused append (kv_new == nullptr: off)
+    const void* kv_new; long long kn_sb;
+    const void* pe_new; long long pn_sb;
+    void* kv_dst; long long kd_sb, kd_st;
+    void* pe_dst; long long pd_sb, pd_st;
     void* qt;
     int32_t* list;
     int32_t* counts;
     uint32_t* status;
 };
+
+// Eight consecutive elements as fp32 (16 or 32 bytes, aligned), and back.
+template <typename T> __device__ __forceinline__ void load8f(const T* p, float (&v)[8]);
+template <> __device__ __forceinline__ void load8f<bf16>(const bf16* p, float (&v)[8]) {
+    const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+}
+template <> __device__ __forceinline__ void load8f<float>(const float* p, float (&v)[8]) {
+    const f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = x0[e]; v[4 + e] = x1[e]; }
+}
+template <typename T> __device__ __forceinline__ void store8f(T* p, const float (&v)[8]);
+template <> __device__ __forceinline__ void store8f<bf16>(bf16* p, const float (&v)[8]) {
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = f2bf(v[e]);
+    *(bf16x8*)p = x;
+}
+template <> __device__ __forceinline__ void store8f<float>(float* p, const float (&v)[8]) {
+    f32x4 x0, x1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x0[e] = v[e]; x1[e] = v[4 + e]; }
+    *(f32x4*)p = x0;
+    *(f32x4*)(p + 4) = x1;
+}
+
+// The new token's row: kv_cache[b][p] = kv_new[b] (16-byte copies by the
+// first threads) and pe_cache[b][p] = pe_new[b] rotated at p, interleaved
+// pairs, by threads 128..135 (8 features = 4 pairs each; cs is table row p).
+template <typename ActT>
+__device__ void append_row(const PrepArgs& a, int b, int p, const float* cs) {
+    const int tid = threadIdx.x;
+    constexpr int PER = 16 / (int)sizeof(ActT);       // elements per 16 bytes
+    if (tid < RANK / PER) {
+        const ActT* src = (const ActT*)a.kv_new + b * a.kn_sb;
+        ActT* dst = (ActT*)a.kv_dst + b * a.kd_sb + (long long)p * a.kd_st;
+        *(u32x4*)(dst + tid * PER) = *(const u32x4*)(src + tid * PER);
+    } else if (tid >= 128 && tid < 128 + D_ROPE / 8) {
+        const int q = tid - 128;
+        float v[8], o[8];
+        load8f<ActT>((const ActT*)a.pe_new + b * a.pn_sb + 8 * q, v);
+        const f32x4 c0 = *(const f32x4*)(cs + 8 * q), c1 = *(const f32x4*)(cs + 8 * q + 4);
+        const float cc[4] = {c0[0], c0[2], c1[0], c1[2]}, ss[4] = {c0[1], c0[3], c1[1], c1[3]};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o[2 * j] = v[2 * j] * cc[j] - v[2 * j + 1] * ss[j];
+            o[2 * j + 1] = v[2 * j] * ss[j] + v[2 * j + 1] * cc[j];
+        }
+        store8f<ActT>((ActT*)a.pe_dst + b * a.pd_sb + (long long)p * a.pd_st + 8 * q, o);
+    }
+}
 
 // Longest compacted list built in LDS (it overwrites the 64 KB bitmap area).
 constexpr int PREP_LIST_MAX = 16384;
@@ -189,6 +247,9 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
             t[4 * k] = v[0]; t[4 * k + 1] = v[1]; t[4 * k + 2] = v[2]; t[4 * k + 3] = v[3];
         }
     }
+    // -- fused append of the new row (before any position is read: the
+    // attention kernel runs after this one) --
+    if (a.kv_new && L >= 1 && L <= a.Lmax && L <= a.Trope) append_row<ActT>(a, b, L - 1, cs);
     // -- selection --
     uint32_t status = 0;
     if (L < 1 || L > a.Lmax || L > a.Trope) status |= BAD_CACHE_LEN;
@@ -474,6 +535,10 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     a.w_uk = p.w_uk; a.wk_sh = p.w_uk_stride_h;
     a.idx = p.topk_indices; a.idx_sb = p.idx_stride_b;
     a.cache_lens = p.cache_lens; a.rope_table = p.rope_table;
+    a.kv_new = p.kv_new; a.kn_sb = p.kv_new_stride_b;
+    a.pe_new = p.pe_new; a.pn_sb = p.pe_new_stride_b;
+    a.kv_dst = const_cast<void*>(p.kv_cache); a.kd_sb = p.kv_stride_b; a.kd_st = p.kv_stride_t;
+    a.pe_dst = const_cast<void*>(p.pe_cache); a.pd_sb = p.pe_stride_b; a.pd_st = p.pe_stride_t;
     a.qt = w.qt; a.list = w.list; a.counts = w.counts; a.status = w.status;
     const dim3 grid(a.n_absorb + p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;

@@ -54,7 +54,9 @@ class DecodeParams(ctypes.Structure):
                 ("lse_out", _P),
                 ("workspace", _P), ("workspace_size", ctypes.c_size_t),
                 ("profile_events", _P),
-                ("validate_status", ctypes.c_uint32), ("reserved0", ctypes.c_uint32)]
+                ("validate_status", ctypes.c_uint32), ("reserved0", ctypes.c_uint32),
+                ("kv_new", _P), ("kv_new_stride_b", _I64),
+                ("pe_new", _P), ("pe_new_stride_b", _I64)]
 
 
 class TopkParams(ctypes.Structure):
@@ -182,8 +184,10 @@ def _inner_contig(name, t, width):
 
 def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
                  softmax_scale, out, lse=None, workspace=None, num_splits=0, num_cus=0, validate=False,
-                 events=None) -> DecodeParams:
-    """Fill mla_decode_params_t from torch tensors (shapes as in the header)."""
+                 events=None, kv_new=None, pe_new=None) -> DecodeParams:
+    """Fill mla_decode_params_t from torch tensors (shapes as in the header).
+    kv_new [B, 512] and pe_new [B, 64] (both or neither) switch on the fused
+    append of each sequence's row p_b = L_b - 1 into kv_cache / pe_cache."""
     torch = _torch()
     B, H = q_nope.shape[0], q_nope.shape[1]
     K = topk_indices.shape[1]
@@ -222,6 +226,15 @@ def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cac
     if workspace is not None:
         p.workspace, p.workspace_size = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     p.profile_events = events
+    if (kv_new is None) != (pe_new is None):
+        raise ValueError("kv_new and pe_new go together")
+    if kv_new is not None:
+        _inner_contig("kv_new", kv_new, 512)
+        _inner_contig("pe_new", pe_new, 64)
+        if kv_new.dtype != kv_cache.dtype or pe_new.dtype != kv_cache.dtype:
+            raise TypeError("kv_new / pe_new must have the caches' dtype")
+        p.kv_new, p.kv_new_stride_b = kv_new.data_ptr(), kv_new.stride(0)
+        p.pe_new, p.pe_new_stride_b = pe_new.data_ptr(), pe_new.stride(0)
     return p
 
 
@@ -235,8 +248,9 @@ def decode_attn(params: DecodeParams, stream=None, check=True) -> int:
 
 def decode(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
            softmax_scale, out=None, lse=None, workspace=None, out_dtype=None, num_splits=0,
-           validate=False, stream=None, with_lse=True):
-    """Allocate what is missing, run one decode step; returns (out, lse)."""
+           validate=False, stream=None, with_lse=True, kv_new=None, pe_new=None):
+    """Allocate what is missing, run one decode step; returns (out, lse).
+    With kv_new / pe_new the step first appends each sequence's new row."""
     torch = _torch()
     B, H = q_nope.shape[0], q_nope.shape[1]
     if out is None:
@@ -249,7 +263,8 @@ def decode(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_len
             raise MLAError(MLA_ERR_INVALID_ARG, "no workspace size for these sizes")
         workspace = torch.empty(n, dtype=torch.uint8, device=q_nope.device)
     p = build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
-                     softmax_scale, out, lse, workspace, num_splits=num_splits, validate=validate)
+                     softmax_scale, out, lse, workspace, num_splits=num_splits, validate=validate,
+                     kv_new=kv_new, pe_new=pe_new)
     decode_attn(p, stream)
     return out, lse
 

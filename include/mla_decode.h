@@ -168,6 +168,21 @@ typedef struct mla_decode_params {
     /* validate mode output: OR of MLA_BAD_* bits (0 when every row is valid) */
     uint32_t validate_status;
     uint32_t reserved0;
+
+    /* optional fused append of the new token's row [page "Query rotary
+     * features", excerpt mla-init: the joint down-projection emits the
+     * latent and one shared rotary key].  Both NULL: the caches are only
+     * read.  Both set: kv_new [B][512] (the latent, already normalised) and
+     * pe_new [B][64] (the rotary key before rotation), dtype_act, 16-byte
+     * aligned, batch strides in elements (multiples of 8).  Before any
+     * cached position is read, row p_b = L_b - 1 of each sequence is written:
+     * kv_cache[b][p_b] = kv_new[b] and pe_cache[b][p_b] = pe_new[b] rotated
+     * at p_b (interleaved pairs, as the query).  The caches are then written
+     * through kv_cache and pe_cache, which must be writable device memory;
+     * a sequence whose L_b is invalid (see MLA_BAD_CACHE_LEN) is not
+     * written. */
+    const void* kv_new;  int64_t kv_new_stride_b;
+    const void* pe_new;  int64_t pe_new_stride_b;
 } mla_decode_params_t;
 
 /*
@@ -193,7 +208,8 @@ size_t mla_decode_workspace_size(int B, int H, int K, int dtype_act, int dtype_w
  * Enqueues MLA_NUM_KERNELS kernels on `stream`:
  *   1. selection compaction (per sequence: drops -1 slots, duplicates and
  *      out-of-range entries, sorts the set ascending), query rotation at
- *      p_b, and the W_UK absorption into Q~ = [q_abs ; q^];
+ *      p_b, the W_UK absorption into Q~ = [q_abs ; q^], and, when kv_new
+ *      is set, the write of each sequence's new row p_b into the caches;
  *   2. split-KV attention over the gathered 576-wide rows (bf16 MFMA,
  *      fp32 accumulation and online softmax) -- or fp32 arithmetic when
  *      dtype_act is F32;

@@ -177,3 +177,19 @@ def test_rope_apply_host_checks_size_and_alias(mla):
     p = _rope_params(mla, y=1 << 20, y_stride_n=512)
     assert mla.lib().mla_rope_apply(ctypes.byref(p), None) == mla.MLA_ERR_INVALID_ARG
     assert mla.lib().mla_rope_apply(None, None) == mla.MLA_ERR_INVALID_ARG
+
+
+_APPEND_OK = dict(kv_new=1 << 21, kv_new_stride_b=512, pe_new=1 << 22, pe_new_stride_b=64)
+
+
+@pytest.mark.parametrize("change,code", [
+    ({}, 3),                                              # valid append fields: fails later, on the workspace
+    ({"pe_new": 0}, 1), ({"kv_new": 0}, 1),               # only one of the pair
+    ({"kv_new": (1 << 21) + 8}, 1), ({"pe_new": (1 << 22) + 4}, 1),
+    ({"kv_new_stride_b": 500}, 1), ({"pe_new_stride_b": 60}, 1), ({"kv_new_stride_b": 4}, 1),
+    ({"pe_new_stride_b": -8}, 1),
+])
+def test_append_host_checks(mla, change, code):
+    p = _params(mla, **{**_APPEND_OK, **change})
+    rc = mla.lib().mla_decode_attn(ctypes.byref(p), None)
+    assert rc == code, mla.last_error()

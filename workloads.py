@@ -156,6 +156,15 @@ def build(name, B, H, cache_lens, K, dtype_act, dtype_w, rope, seed, L_max=None,
     return w
 
 
+def new_rows(B: int, dtype_act: str, seed: int):
+    """The new token's latent [B, 512] and raw rotary key [B, 64] for a fused
+    append, drawn like the cached rows (N(0, 1), rounded to bf16 for bf16
+    activations)."""
+    rng = np.random.default_rng(seed)
+    act = round_bf16 if dtype_act == "bf16" else (lambda a: a)
+    return act(_normal(rng, (B, KV_RANK))), act(_normal(rng, (B, D_ROPE)))
+
+
 def workload(name: str, batch_limit: int | None = None) -> Workload:
     """The named workload (tiny, page, batched, long, ragged).  ``batch_limit``
     draws a smaller batch with the same recipe and seed (its values differ
