@@ -109,6 +109,135 @@ def cpu_baseline(w, budget_s):
                       f"fp64 non-absorbed definition over the selected rows ({dt:.1f} s)"}
 
 
+def _timed_launches(fn, K, warmup):
+    """Average duration (ms) of fn() over K launches, from HIP events on the
+    launching stream (torch's current stream), after warmup launches."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / K
+    return sum(a.elapsed_time(b) for a, b in ev) / K, wall
+
+
+def bench_op(args):
+    """One JSON line for one of the adjacent entry points (not the decode
+    step): top-k selection, rotary apply, or the decode step with the fused
+    append switched on."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads as W
+    from decode_attention_absorbed_amd import mla
+
+    torch.cuda.set_device(0)
+    K, warm = args.steps, args.warmup
+    rng = np.random.default_rng(2024)
+    line = {"n_gpus": 1, "steps": K, "warmup": warm, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "data": "synthetic"}
+    if args.op == "topk":
+        # the long-context indexer output: 64 sequences x 16384 scores, k = 2048
+        B, L, k = 64, 16384, 2048
+        scores_np = rng.standard_normal((B, L)).astype(np.float32)
+        reps = [torch.from_numpy(scores_np).cuda() for _ in range(8)]
+        lens = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        outs = torch.empty((B, k), dtype=torch.int32, device="cuda")
+        it = [0]
+
+        def fn():
+            mla.topk(reps[it[0] % 8], lens, k, out=outs)
+            it[0] += 1
+        ms, wall = _timed_launches(fn, K, warm)
+        nbytes = B * L * 4 + B * k * 4
+        t0, n = time.perf_counter(), 0
+        while n < B and time.perf_counter() - t0 < args.cpu_budget:
+            oracle.topk_select(scores_np[n].astype(np.float64), L, k)
+            n += 1
+        cpu = {"value": n / (time.perf_counter() - t0), "unit": "sequences/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} of {B} score rows"}
+        line.update(metric="top-k selection sequences/s", value=B / (ms * 1e-3), unit="sequences/s",
+                    ms_per_step=ms, wall_ms_per_launch=wall, dtype="f32",
+                    config={"workload": f"top-k: B={B} rows of L={L} fp32 scores, k={k}"},
+                    roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "traffic": None, "kernel": "topk_kernel", "algorithmic_bytes": nbytes},
+                    cpu_baseline=cpu)
+    elif args.op == "rope":
+        # a prefill chunk of 16384 tokens at positions 0..16383, 64 heads of
+        # 64 rotary features each (the indexer's query shape), bf16
+        T, Hh = 16384, 64
+        N = T * Hh
+        table = mla.rope_freqs(W.ROPE_YARN)
+        xs = [torch.from_numpy(rng.standard_normal((T, Hh, 64)).astype(np.float32)).cuda().to(torch.bfloat16)
+              for _ in range(2)]
+        pos = torch.arange(T, dtype=torch.int32, device="cuda")
+        ys = [torch.empty_like(x) for x in xs]
+        it = [0]
+
+        def fn():
+            i = it[0] % 2
+            mla.rope_apply(xs[i], pos, table, args.rope_layout == "interleaved", out=ys[i])
+            it[0] += 1
+        ms, wall = _timed_launches(fn, K, warm)
+        # read + write every vector; the table row (256 B) and position of each token once
+        nbytes = N * 64 * 2 * 2 + T * (256 + 4)
+        xc = xs[0].reshape(N, 64)[:4096].float().cpu().numpy().astype(np.float64)
+        pc = np.repeat(np.arange(T), Hh)[:4096]
+        f = oracle.rope_rotate if args.rope_layout == "interleaved" else oracle.rope_rotate_halves
+        cfg = oracle.RopeConfig(**W.ROPE_YARN)
+        t0, n = time.perf_counter(), 0
+        while n < 4096 and time.perf_counter() - t0 < args.cpu_budget:
+            f(xc[n], int(pc[n]), cfg)
+            n += 1
+        cpu = {"value": n / (time.perf_counter() - t0), "unit": "vectors/s", "cores": 1, "kind": "oracle",
+               "sample": f"first {n} vectors"}
+        line.update(metric="rotary apply vectors/s", value=N / (ms * 1e-3), unit="vectors/s", ms_per_step=ms,
+                    wall_ms_per_launch=wall, dtype="bf16",
+                    config={"workload": f"rope: {T} tokens x {Hh} heads of 64 bf16 features at positions "
+                                        f"0..{T - 1}, {args.rope_layout} layout"},
+                    roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "traffic": None, "kernel": "rope_apply_kernel", "algorithmic_bytes": nbytes},
+                    cpu_baseline=cpu)
+    else:
+        # the decode step on the ragged batch, with and without the fused append
+        w = W.workload("ragged")
+        dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+        act, wt = torch.bfloat16, torch.float32
+        t = dict(q_nope=dev(w.q_nope, act), q_pe=dev(w.q_pe, act), w_uk=dev(w.w_uk, wt), w_uv=dev(w.w_uv, wt),
+                 kv=dev(w.kv_cache, act), pe=dev(w.pe_cache, act))
+        idx = torch.from_numpy(w.topk_indices).cuda()
+        lens = torch.from_numpy(w.cache_lens).cuda()
+        kv_new, pe_new = (dev(a, act) for a in W.new_rows(w.B, "bf16", 2025))
+        table = mla.rope_freqs(w.rope)
+        scale = mla.softmax_scale(192, w.rope)
+        out = torch.empty((w.B, w.H, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(mla.workspace_size(w.B, w.H, w.K, 1, 0), dtype=torch.uint8, device="cuda")
+        ps = {name: mla.build_params(t["q_nope"], t["q_pe"], t["w_uk"], t["w_uv"], t["kv"], t["pe"], idx, lens,
+                                     table, scale, out, lse, ws, **extra)
+              for name, extra in (("off", {}), ("on", dict(kv_new=kv_new, pe_new=pe_new)))}
+        # the two modes alternate in rounds so that neither runs colder
+        res = {"off": [], "on": []}
+        for _ in range(4):
+            for name, p in ps.items():
+                res[name].append(_timed_launches(lambda: mla.decode_attn(p), max(K // 4, 1), warm)[0])
+        res = {k: float(np.mean(v)) for k, v in res.items()}
+        line.update(metric="MLA decode step with fused cache append, tokens/s", value=w.B / (res["on"] * 1e-3),
+                    unit="tokens/s", ms_per_step=res["on"], ms_per_step_without_append=res["off"], dtype="bf16",
+                    config={"workload": "ragged decode step (B=128, H=128, L_b~U{1024..16384}, top-k 2048) "
+                                        "plus the append of one row per sequence",
+                            "inputs_resident": "one copy (L2 / Infinity Cache may hold part of it)"})
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,7 +250,16 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input copies cycled (0 = enough for 1.5 GB)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--op", default="decode", choices=["decode", "topk", "rope", "append"],
+                    help="decode: the decode step (default); others time an adjacent entry point")
+    ap.add_argument("--rope-layout", default="halves", choices=["halves", "interleaved"])
     args = ap.parse_args()
+    if args.op != "decode":
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_op(args)
+        return
     if args.copy_calibration:
         import torch
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB

@@ -28,7 +28,7 @@ constexpr int kMaxBatch = 1 << 20;
 constexpr int kMaxHeads = 1 << 12;
 constexpr int kMaxSplits = 64;
 constexpr int kMaxRopeRows = 1 << 24;
-constexpr long long kMaxRopeVectors = 1ll << 27;   // 8 threads each: the grid stays below 2^31
+constexpr long long kMaxRopeVectors = 1ll << 27;   // 4 threads each: the grid stays below 2^31
 
 int query_num_cus(int* out) {
     int dev = 0;

@@ -6,10 +6,10 @@
 // halves ((i, i+32): the vector is read as [2][32] and transposed, and the
 // real parts come back first).
 //
-// Work unit: 4 pairs per thread, 8 threads per vector.  Interleaved: the
-// thread owns 8 contiguous features; halves: 4 contiguous features in each
-// half.  Each thread reads its features and the 4 (cos, sin) entries, then
-// writes the same features, so y may alias x.  A position outside the
+// Work unit: 8 pairs per thread, 4 threads per vector.  Interleaved: the
+// thread owns 16 contiguous features; halves: 8 contiguous features in each
+// half (16-byte accesses for bf16).  Each thread reads its features and
+// their 8 (cos, sin) entries, then writes the same features, so y may alias x.  A position outside the
 // table writes NaN to the whole vector.
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
@@ -25,78 +25,89 @@ struct RopeApplyArgs {
     const float* table;
 };
 
-template <typename T> struct Vec4;
-template <> struct Vec4<bf16>  { using type = bf16x4; };
-template <> struct Vec4<float> { using type = float4; };
+// Eight consecutive elements as fp32 (16 or 32 bytes, aligned), and back.
+template <typename T> __device__ __forceinline__ void ld8(const T* p, float (&v)[8]);
+template <> __device__ __forceinline__ void ld8<bf16>(const bf16* p, float (&v)[8]) {
+    const bf16x8 x = *(const bf16x8*)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+}
+template <> __device__ __forceinline__ void ld8<float>(const float* p, float (&v)[8]) {
+    const f32x4 x0 = *(const f32x4*)p, x1 = *(const f32x4*)(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { v[e] = x0[e]; v[4 + e] = x1[e]; }
+}
+template <typename T> __device__ __forceinline__ void st8(T* p, const float (&v)[8]);
+template <> __device__ __forceinline__ void st8<bf16>(bf16* p, const float (&v)[8]) {
+    bf16x8 x;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = f2bf(v[e]);
+    *(bf16x8*)p = x;
+}
+template <> __device__ __forceinline__ void st8<float>(float* p, const float (&v)[8]) {
+    f32x4 x0, x1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x0[e] = v[e]; x1[e] = v[4 + e]; }
+    *(f32x4*)p = x0;
+    *(f32x4*)(p + 4) = x1;
+}
 
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float (&v)[4]) {
-    const auto r = *reinterpret_cast<const typename Vec4<T>::type*>(p);
-    v[0] = to_f32<T>(r[0]); v[1] = to_f32<T>(r[1]); v[2] = to_f32<T>(r[2]); v[3] = to_f32<T>(r[3]);
-}
-template <>
-__device__ __forceinline__ void load4<float>(const float* p, float (&v)[4]) {
-    const float4 r = *reinterpret_cast<const float4*>(p);
-    v[0] = r.x; v[1] = r.y; v[2] = r.z; v[3] = r.w;
-}
-template <typename T>
-__device__ __forceinline__ void store4(T* p, const float (&v)[4]) {
-    typename Vec4<T>::type r;
-    r[0] = from_f32<T>(v[0]); r[1] = from_f32<T>(v[1]); r[2] = from_f32<T>(v[2]); r[3] = from_f32<T>(v[3]);
-    *reinterpret_cast<typename Vec4<T>::type*>(p) = r;
-}
-template <>
-__device__ __forceinline__ void store4<float>(float* p, const float (&v)[4]) {
-    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-}
-
+// Thread q (0..3) of a vector owns pairs 8q .. 8q+7.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_apply_kernel(RopeApplyArgs a) {
     const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
-    const long long v = g >> 3;                  // vector
+    const long long v = g >> 2;                  // vector
     if (v >= a.NH) return;
-    const int part = (int)(g & 7);               // pairs 4 part .. 4 part + 3
+    const int q = (int)(g & 3);
     const long long n = v / a.H;
     const int h = (int)(v - n * a.H);
     const T* x = static_cast<const T*>(a.x) + n * a.xs_n + h * a.xs_h;
     T* y = static_cast<T*>(a.y) + n * a.ys_n + h * a.ys_h;
     const int t = a.positions[n];
 
-    // first and second members of the 4 pairs
-    float re[4], im[4];
+    float re[8], im[8];                          // first and second members of the 8 pairs
     if (a.interleaved) {
-        float lo[4], hi[4];
-        load4<T>(x + 8 * part, lo);
-        load4<T>(x + 8 * part + 4, hi);
-        re[0] = lo[0]; im[0] = lo[1]; re[1] = lo[2]; im[1] = lo[3];
-        re[2] = hi[0]; im[2] = hi[1]; re[3] = hi[2]; im[3] = hi[3];
-    } else {
-        load4<T>(x + 4 * part, re);
-        load4<T>(x + 32 + 4 * part, im);
-    }
-    float o_re[4], o_im[4];
-    if (t >= 0 && t < a.table_len) {
-        const float4* cs = reinterpret_cast<const float4*>(a.table + ((long long)t * 32 + 4 * part) * 2);
-        const float4 c01 = cs[0], c23 = cs[1];   // (cos, sin) of pairs 4 part + {0, 1}, then {2, 3}
-        const float c[4] = {c01.x, c01.z, c23.x, c23.z};
-        const float s[4] = {c01.y, c01.w, c23.y, c23.w};
+        float lo[8], hi[8];
+        ld8<T>(x + 16 * q, lo);
+        ld8<T>(x + 16 * q + 8, hi);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            o_re[j] = re[j] * c[j] - im[j] * s[j];
-            o_im[j] = re[j] * s[j] + im[j] * c[j];
+            re[j] = lo[2 * j]; im[j] = lo[2 * j + 1];
+            re[4 + j] = hi[2 * j]; im[4 + j] = hi[2 * j + 1];
+        }
+    } else {
+        ld8<T>(x + 8 * q, re);
+        ld8<T>(x + 32 + 8 * q, im);
+    }
+    float o_re[8], o_im[8];
+    if (t >= 0 && t < a.table_len) {
+        const f32x4* cs = reinterpret_cast<const f32x4*>(a.table + ((long long)t * 32 + 8 * q) * 2);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const f32x4 c = cs[k];               // (cos, sin) of pairs 8q + 2k and 8q + 2k + 1
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int j = 2 * k + e;
+                o_re[j] = re[j] * c[2 * e] - im[j] * c[2 * e + 1];
+                o_im[j] = re[j] * c[2 * e + 1] + im[j] * c[2 * e];
+            }
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) o_re[j] = o_im[j] = __builtin_nanf("");
+        for (int j = 0; j < 8; ++j) o_re[j] = o_im[j] = __builtin_nanf("");
     }
     if (a.interleaved) {
-        const float lo[4] = {o_re[0], o_im[0], o_re[1], o_im[1]};
-        const float hi[4] = {o_re[2], o_im[2], o_re[3], o_im[3]};
-        store4<T>(y + 8 * part, lo);
-        store4<T>(y + 8 * part + 4, hi);
+        float lo[8], hi[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            lo[2 * j] = o_re[j]; lo[2 * j + 1] = o_im[j];
+            hi[2 * j] = o_re[4 + j]; hi[2 * j + 1] = o_im[4 + j];
+        }
+        st8<T>(y + 16 * q, lo);
+        st8<T>(y + 16 * q + 8, hi);
     } else {
-        store4<T>(y + 4 * part, o_re);
-        store4<T>(y + 32 + 4 * part, o_im);
+        st8<T>(y + 8 * q, o_re);
+        st8<T>(y + 32 + 8 * q, o_im);
     }
 }
 
@@ -106,7 +117,7 @@ hipError_t launch_rope_apply(int N, int H, bool bf16_io, bool interleaved, int t
                              const int32_t* positions, const float* table, hipStream_t s) {
     RopeApplyArgs a{(long long)N * H, H, interleaved ? 1 : 0, table_len, x, xs_n, xs_h, y, ys_n, ys_h,
                     positions, table};
-    const long long threads = a.NH * 8;
+    const long long threads = a.NH * 4;
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     if (bf16_io) hipLaunchKernelGGL(rope_apply_kernel<bf16>, dim3(blocks), dim3(256), 0, s, a);
     else         hipLaunchKernelGGL(rope_apply_kernel<float>, dim3(blocks), dim3(256), 0, s, a);

@@ -12,11 +12,17 @@
 // are taken.
 //
 // One workgroup (16 waves) per sequence.  Scores become order-preserving
-// 32-bit keys; a radix select over four 8-bit digits, most significant
-// first, finds the threshold key T and how many keys equal to T are taken
-// (256-bin LDS histograms of the keys that share the prefix found so far,
-// one per wave and then summed, so that the many keys of one digit value
-// do not all collide on one LDS word).
+// 32-bit keys; a radix select over three digits, most significant first
+// (bits 31..21, 20..10, 9..0), finds the threshold key T and how many keys
+// equal to T are taken.  Each pass builds an LDS histogram of the keys that
+// share the prefix found so far and locates the bin holding the k-th
+// largest with a block-wide scan.  The first digit spans the sign, the
+// exponent and two mantissa bits, so that keys of similar magnitude spread
+// over several bins (same-address LDS atomics within one instruction
+// serialise); the first pass also uses two histogram copies, one per half
+// of the waves.  The keys that fall in the first pass's threshold bin are
+// then gathered into a short LDS list (when there are at most 2048 of them),
+// so that the later passes visit only those.
 // The keys live in LDS when the row fits (up to 32768 positions), otherwise
 // every pass re-reads the row (it stays in L2).  The output pass gives each
 // wave a contiguous range of positions, visits it 64 positions at a time
@@ -27,7 +33,10 @@
 namespace mla {
 
 constexpr int TK_THREADS = 1024;
+constexpr int TK_WAVES = TK_THREADS / 64;
 constexpr int TK_LDS_KEYS = 32768;          // 128 KB of keys in LDS
+constexpr int TK_BINS = 2048;               // widest digit: 11 bits
+constexpr int TK_CAND = TK_BINS;            // candidate list (aliases the second histogram copy)
 
 struct TopkArgs {
     int B, k, max_len;
@@ -47,10 +56,10 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 
 __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     __shared__ uint32_t keys[TK_LDS_KEYS];
-    __shared__ int whist[TK_THREADS / 64][256];   // per-wave histograms (fewer colliding atomics)
-    __shared__ int hist[256];
-    __shared__ int wcnt[2][TK_THREADS / 64];
-    __shared__ int sel_digit, sel_above;
+    __shared__ int hist[2][TK_BINS];
+    __shared__ int wsum[TK_WAVES];
+    __shared__ int wcnt[2][TK_WAVES];
+    __shared__ int sel_digit, sel_above, sel_count, ncand;
     const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* row = a.scores + (long long)b * a.score_stride;
     int32_t* out = a.out + (long long)b * a.out_stride;
@@ -92,52 +101,83 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
             }
         }
     }
+    if (tid == 0) ncand = 0;
+    uint32_t* cand = (uint32_t*)&hist[1][0];
 
-    // radix select: after the pass at shift s, prefix holds the top 32 - s
-    // bits of T, and krem the number of keys equal to that prefix still to
-    // take (keys above the prefix are all taken)
+    // radix select: after each pass, prefix holds the leading bits of T
+    // (pmask marks them), and krem the number of keys equal to that prefix
+    // still to take (keys above the prefix are all taken)
     uint32_t prefix = 0u, pmask = 0u;
     int krem = kb;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < (TK_THREADS / 64) * 256; i += TK_THREADS) (&whist[0][0])[i] = 0;
+    bool use_cand = false;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        const int ncopy = pass == 0 ? 2 : 1;
+        for (int i = tid; i < ncopy * TK_BINS; i += TK_THREADS) (&hist[0][0])[i] = 0;
         __syncthreads();
-        visit8(tid, TK_THREADS, [&](uint32_t key, int i) {
-            if (i < L && (key & pmask) == prefix) atomicAdd(&whist[wave][(key >> shift) & 255], 1);
-        });
-        __syncthreads();
-        if (tid < 256) {
-            int c = 0;
-#pragma unroll
-            for (int w = 0; w < TK_THREADS / 64; ++w) c += whist[w][tid];
-            hist[tid] = c;
+        if (pass == 0) {
+            int* h = hist[wave & 1];
+            visit8(tid, TK_THREADS, [&](uint32_t key, int i) {
+                if (i < L) atomicAdd(&h[key >> 21], 1);
+            });
+        } else if (use_cand) {
+            for (int i = tid; i < ncand; i += TK_THREADS) {
+                const uint32_t key = cand[i];
+                if ((key & pmask) == prefix) atomicAdd(&hist[0][(key >> shift) & (nb - 1)], 1);
+            }
+        } else {
+            visit8(tid, TK_THREADS, [&](uint32_t key, int i) {
+                if (i < L && (key & pmask) == prefix) atomicAdd(&hist[0][(key >> shift) & (nb - 1)], 1);
+            });
         }
         __syncthreads();
-        if (tid < 64) {
-            // suffix sums over the 256 bins, 4 bins per lane (lane 0 holds
-            // the top bins 255..252)
-            int c[4], s = 0;
+        // thread t holds bins nb-1-2t and nb-2-2t (t < nb/2); an inclusive
+        // scan over t gives the keys in higher bins
+        int c0 = 0, c1 = 0;
+        if (tid < nb / 2) {
+            const int b0 = nb - 1 - 2 * tid;
+            c0 = hist[0][b0] + (pass == 0 ? hist[1][b0] : 0);
+            c1 = hist[0][b0 - 1] + (pass == 0 ? hist[1][b0 - 1] : 0);
+        }
+        int inc = c0 + c1;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) { c[j] = hist[255 - (4 * tid + j)]; s += c[j]; }
-            int inc = s;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int n = __shfl_up(inc, o);
-                if (tid >= o) inc += n;
-            }
-            int above = inc - s;                 // keys in bins above this lane's four
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (above < krem && above + c[j] >= krem) {
-                    sel_digit = 255 - (4 * tid + j);
-                    sel_above = above;
-                }
-                above += c[j];
+        for (int o = 1; o < 64; o <<= 1) {
+            const int n = __shfl_up(inc, o);
+            if (lane >= o) inc += n;
+        }
+        if (lane == 63) wsum[wave] = inc;
+        __syncthreads();
+        int above = inc - c0 - c1;
+        for (int w = 0; w < wave; ++w) above += wsum[w];
+        if (tid < nb / 2) {
+            if (above < krem && above + c0 >= krem) {
+                sel_digit = nb - 1 - 2 * tid; sel_above = above; sel_count = c0;
+            } else if (above + c0 < krem && above + c0 + c1 >= krem) {
+                sel_digit = nb - 2 - 2 * tid; sel_above = above + c0; sel_count = c1;
             }
         }
         __syncthreads();
         prefix |= (uint32_t)sel_digit << shift;
-        pmask |= 255u << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
         krem -= sel_above;
+        if (pass == 0 && sel_count <= TK_CAND) {
+            // gather the keys of the threshold bin (the histogram copy it
+            // overwrites was last read before the barrier above)
+            use_cand = true;
+            visit8(tid, TK_THREADS, [&](uint32_t key, int i) {
+                const bool hit = i < L && (key >> 21) == (prefix >> 21);
+                const uint64_t m = __ballot(hit);
+                if (m) {
+                    int base = 0;
+                    if (lane == 0) base = atomicAdd(&ncand, __popcll(m));
+                    base = __shfl(base, 0);
+                    if (hit) cand[base + __popcll(m & ((1ull << lane) - 1ull))] = key;
+                }
+            });
+            __syncthreads();
+        }
     }
     const uint32_t T = prefix;                   // krem keys equal to T are taken
 
@@ -198,10 +238,185 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(TopkArgs a) {
     for (int i = kb + tid; i < a.k; i += TK_THREADS) out[i] = -1;
 }
 
+// ---------------------------------------------------------------------------
+// Rows of at most 32 * 1024 positions: thread t keeps the keys of positions
+// [C t, C t + C) in registers (C = 16 or 32), so the passes read no LDS for
+// keys.  The histograms are four LDS copies (one per group of four waves);
+// the candidate list is its own LDS array.  The output is one block-wide
+// scan of each thread's (above T, equal to T) counts, after which every
+// thread writes its selected positions in order.
+// ---------------------------------------------------------------------------
+constexpr int TK_COPIES = 4;
+
+// Thread t holds bins nb-1-2t and nb-2-2t (summed over the copies); a
+// block-wide inclusive scan over t counts the keys in higher bins.  The
+// thread whose bins contain the krem-th largest key records the digit, the
+// number of keys above it and the digit's own count in sel[0..2].
+__device__ __forceinline__ void find_digit(const int (*hist)[TK_BINS], int nb, int krem, int* wsum, int* sel) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int c0 = 0, c1 = 0;
+    if (tid < nb / 2) {
+        const int b0 = nb - 1 - 2 * tid;
+#pragma unroll
+        for (int c = 0; c < TK_COPIES; ++c) { c0 += hist[c][b0]; c1 += hist[c][b0 - 1]; }
+    }
+    int inc = c0 + c1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int n = __shfl_up(inc, o);
+        if (lane >= o) inc += n;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int above = inc - c0 - c1;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) above += w < wave ? wsum[w] : 0;   // independent reads
+    if (tid < nb / 2) {
+        if (above < krem && above + c0 >= krem) {
+            sel[0] = nb - 1 - 2 * tid; sel[1] = above; sel[2] = c0;
+        } else if (above + c0 < krem && above + c0 + c1 >= krem) {
+            sel[0] = nb - 2 - 2 * tid; sel[1] = above + c0; sel[2] = c1;
+        }
+    }
+}
+
+template <int C>
+__global__ __launch_bounds__(TK_THREADS) void topk_reg_kernel(TopkArgs a) {
+    // two histogram sets: passes 0 and 2 use set 0, pass 1 set 1, so that
+    // set 0 is cleared again while pass 1 runs
+    __shared__ int hist[2][TK_COPIES][TK_BINS];
+    __shared__ uint32_t cand[TK_CAND];
+    __shared__ int wsum[TK_WAVES];
+    __shared__ int sel[3];
+    __shared__ int ncand;
+    const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float* row = a.scores + (long long)b * a.score_stride;
+    int32_t* out = a.out + (long long)b * a.out_stride;
+    const int L = min(max(a.cache_lens[b], 0), a.max_len);
+    const int kb = min(a.k, L);
+    if (kb == L) {
+        for (int i = tid; i < a.k; i += TK_THREADS) out[i] = i < L ? i : -1;
+        return;
+    }
+    const int p0 = tid * C;
+    const int nv = min(max(L - p0, 0), C);            // this thread's positions below L
+    float sc[C];
+    if (nv == C && ((uintptr_t)row & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < C / 4; ++q) {
+            const f32x4 v = *(const f32x4*)(row + p0 + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[4 * q + e] = v[e];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < C; ++j) sc[j] = j < nv ? row[p0 + j] : 0.f;
+    }
+    // cleared while the scores are in flight
+    for (int i = tid; i < 2 * TK_COPIES * TK_BINS; i += TK_THREADS) (&hist[0][0][0])[i] = 0;
+    if (tid == 0) ncand = 0;
+    uint32_t key[C];
+#pragma unroll
+    for (int j = 0; j < C; ++j) key[j] = score_key(sc[j]);
+    __syncthreads();
+
+    uint32_t prefix = 0u, pmask = 0u;
+    int krem = kb;
+    bool use_cand = false;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+        const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+        const int nb = pass == 2 ? 1024 : 2048;
+        int (*hs)[TK_BINS] = hist[pass & 1];
+        int* h = hs[wave & (TK_COPIES - 1)];
+        if (use_cand) {
+            for (int i = tid; i < ncand; i += TK_THREADS) {
+                const uint32_t kk = cand[i];
+                if ((kk & pmask) == prefix) atomicAdd(&h[(kk >> shift) & (nb - 1)], 1);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < C; ++j)
+                if (j < nv && (key[j] & pmask) == prefix) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1);
+        }
+        __syncthreads();
+        find_digit(hs, nb, krem, wsum, sel);
+        __syncthreads();
+        prefix |= (uint32_t)sel[0] << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        krem -= sel[1];
+        if (pass == 0) {
+            // set 0 again for pass 2 (its reads ended at the barrier above;
+            // pass 1's barrier orders this before pass 2's atomics)
+            for (int i = tid; i < TK_COPIES * TK_BINS; i += TK_THREADS) (&hist[0][0][0])[i] = 0;
+            if (sel[2] <= TK_CAND) {
+                // the keys of the threshold bin into cand: a wave scan of the
+                // per-thread counts, one LDS atomic per wave for its base
+                use_cand = true;
+                const uint32_t d1 = prefix >> 21;
+                int nh = 0;
+#pragma unroll
+                for (int j = 0; j < C; ++j) nh += (j < nv && (key[j] >> 21) == d1) ? 1 : 0;
+                int inc = nh;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int n = __shfl_up(inc, o);
+                    if (lane >= o) inc += n;
+                }
+                int base = 0;
+                if (lane == 63 && inc > 0) base = atomicAdd(&ncand, inc);
+                base = __shfl(base, 63);
+                int off = base + inc - nh;
+#pragma unroll
+                for (int j = 0; j < C; ++j)
+                    if (j < nv && (key[j] >> 21) == d1) cand[off++] = key[j];
+                __syncthreads();
+            }
+        }
+    }
+    const uint32_t T = prefix;                        // krem keys equal to T are taken
+
+    // counts above and equal to T, packed 16 + 16 bits (L <= 32768: no carry
+    // out of the low half, and the high half stays below 2^16)
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        ngt += (j < nv && key[j] > T) ? 1 : 0;
+        neq += (j < nv && key[j] == T) ? 1 : 0;
+    }
+    const uint32_t v = (uint32_t)ngt | ((uint32_t)neq << 16);
+    uint32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t n = __shfl_up(inc, o);
+        if (lane >= o) inc += n;
+    }
+    if (lane == 63) wsum[wave] = (int)inc;
+    __syncthreads();
+    uint32_t excl = inc - v;
+#pragma unroll
+    for (int w = 0; w < TK_WAVES; ++w) excl += w < wave ? (uint32_t)wsum[w] : 0u;
+    const int gt_before = (int)(excl & 0xFFFFu), eq_before = (int)(excl >> 16);
+    int eq_take = min(neq, max(0, krem - eq_before));  // equal keys this thread takes (lowest first)
+    int off = gt_before + min(eq_before, krem);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+        bool take = j < nv && key[j] > T;
+        if (j < nv && key[j] == T && eq_take > 0) { take = true; --eq_take; }
+        if (take) out[off++] = p0 + j;
+    }
+    for (int i = kb + tid; i < a.k; i += TK_THREADS) out[i] = -1;
+}
+
 hipError_t launch_topk(int B, int k, int max_len, const float* scores, long long score_stride,
                        const int32_t* cache_lens, int32_t* out, long long out_stride, hipStream_t s) {
     TopkArgs a{B, k, max_len, scores, score_stride, cache_lens, out, out_stride};
-    hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(TK_THREADS), 0, s, a);
+    if (max_len <= 16 * TK_THREADS)
+        hipLaunchKernelGGL(topk_reg_kernel<16>, dim3(B), dim3(TK_THREADS), 0, s, a);
+    else if (max_len <= 32 * TK_THREADS)
+        hipLaunchKernelGGL(topk_reg_kernel<32>, dim3(B), dim3(TK_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(TK_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -72,11 +72,43 @@ def test_topk_all_equal_and_k_one():
 
 
 def test_topk_rows_beyond_lds():
-    # rows longer than the 32768 keys kept in LDS re-read the scores each pass
+    # rows longer than 32768 positions (keys re-read from the scores each
+    # pass), and a shorter row of the same launch (keys in LDS)
     rng = np.random.default_rng(1104)
-    B, L, k = 2, 70000, 2048
+    B, L, k = 3, 70000, 2048
     scores = rng.standard_normal((B, L)).astype(np.float32)
-    _check(scores, np.array([70000, 40000]), k, "long rows")
+    _check(scores, np.array([70000, 40000, 20000]), k, "long rows")
+
+
+def test_topk_rows_up_to_32768():
+    # 32 keys per thread: rows in (16384, 32768], with ties, NaN and -0
+    rng = np.random.default_rng(1108)
+    B, L, k = 4, 32768, 2048
+    scores = rng.standard_normal((B, L)).astype(np.float32)
+    scores[2] = rng.integers(-2, 3, size=L).astype(np.float32)
+    scores[2, rng.random(L) < 0.05] = np.nan
+    scores[2, rng.random(L) < 0.1] = -0.0
+    _check(scores, np.array([32768, 20000, 30001, 16385]), k, "32 per thread")
+
+
+def test_topk_all_equal_full_row():
+    # every key equal on a 32768-position row: the packed (above, equal)
+    # counts reach their largest values
+    scores = np.full((2, 32768), 1.5, dtype=np.float32)
+    _check(scores, np.array([32768, 32767]), 100, "all equal 32768")
+
+
+def test_topk_unaligned_rows():
+    # a row stride of L + 1 floats leaves odd rows off 16-byte alignment
+    rng = np.random.default_rng(1109)
+    B, L, k = 4, 3001, 257
+    full = rng.standard_normal((B, L + 1)).astype(np.float32)
+    s = torch.from_numpy(full).cuda()[:, :L]
+    lens = torch.from_numpy(np.array([3001, 3000, 2999, 400], dtype=np.int32)).cuda()
+    got = mla.topk(s, lens, k)
+    torch.cuda.synchronize()
+    want = _expected(full[:, :L].astype(np.float64), [3001, 3000, 2999, 400], k)
+    assert np.array_equal(got.cpu().numpy().astype(np.int64), want)
 
 
 def test_topk_decode_shape_sampled():
