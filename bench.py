@@ -61,6 +61,23 @@ def measured_traffic(workload):
     return e.get("bytes_per_launch")
 
 
+def op_traffic(name, sources):
+    """HBM bytes per launch of an adjacent kernel from the committed counter
+    summary, if it was taken on the current source of that kernel."""
+    path = os.path.join(ROOT, "profiles", "ops_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        e = json.load(f).get(name)
+    h = hashlib.sha256()
+    for src in sources:
+        with open(os.path.join(ROOT, "decode_attention_absorbed_amd", "csrc", src), "rb") as fh:
+            h.update(fh.read())
+    if not e or e.get("source_hash") != h.hexdigest()[:16]:
+        return None
+    return e.get("bytes_per_launch")
+
+
 class Hip:
     """The few HIP runtime calls the bench needs for events."""
 
@@ -167,7 +184,8 @@ def bench_op(args):
                     config={"workload": f"top-k: B={B} rows of L={L} fp32 scores, k={k}"},
                     roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "traffic": None, "kernel": "topk_kernel", "algorithmic_bytes": nbytes},
+                              "traffic": op_traffic("topk", ["mla_topk.hip", "mla_device.hpp"]),
+                              "kernel": "topk_reg_kernel<16>", "algorithmic_bytes": nbytes},
                     cpu_baseline=cpu)
     elif args.op == "rope":
         # a prefill chunk of 16384 tokens at positions 0..16383, 64 heads of
@@ -204,7 +222,8 @@ def bench_op(args):
                                         f"0..{T - 1}, {args.rope_layout} layout"},
                     roofline={"bound": "hbm", "achieved": nbytes / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                               "unit": "GB/s", "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "traffic": None, "kernel": "rope_apply_kernel", "algorithmic_bytes": nbytes},
+                              "traffic": op_traffic("rope_" + args.rope_layout, ["mla_rope.hip", "mla_device.hpp"]),
+                              "kernel": "rope_apply_kernel<bf16>", "algorithmic_bytes": nbytes},
                     cpu_baseline=cpu)
     else:
         # the decode step on the ragged batch, with and without the fused append
