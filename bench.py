@@ -126,6 +126,25 @@ def cpu_baseline(w, budget_s):
                       f"fp64 non-absorbed definition over the selected rows ({dt:.1f} s)"}
 
 
+def stream_copy_gbs(nbytes=1 << 30, reps=10):
+    """Measured device-to-device copy rate (GB/s, bytes read + written),
+    the achievable ceiling beside the 8 TB/s peak."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    rate = 2 * nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return rate
+
+
 def _timed_launches(fn, K, warmup):
     """Average duration (ms) of fn() over K launches, from HIP events on the
     launching stream (torch's current stream), after warmup launches."""
@@ -374,9 +393,12 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    per_kernel = {}
+    per_kernel, spread = {}, {}
     for k, name in enumerate(mla.KERNEL_NAMES):
-        per_kernel[name] = float(np.mean([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in events]))
+        d = np.array([hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for e in events])
+        per_kernel[name] = float(d.mean())
+        spread[name] = {q: float(np.percentile(d, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+    copy_gbs = stream_copy_gbs()
     ms_step = elapsed * 1e3 / K
     t_attn_s = per_kernel["attention"] * 1e-3
     achieved = rows * ROW_BYTES_BF16 / t_attn_s / 1e9 if w.dtype_act == "bf16" else kv_bytes / t_attn_s / 1e9
@@ -403,9 +425,12 @@ def main():
         "hbm_pct_peak_step": kv_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "mfma_tflops_step": flops / (ms_step * 1e-3) / 1e12,
         "kernel_ms": per_kernel,
+        "kernel_ms_spread": spread,
+        "stream_copy_gb_s": copy_gbs,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": tr,
                      "kernel": "attention", "algorithmic_bytes": rows * ROW_BYTES_BF16,
+                     "frac_of_copy": achieved / copy_gbs,
                      "mfma_tflops": 2.0 * w.H * (576 + 512) * rows / t_attn_s / 1e12},
     }
     if not args.no_cpu_baseline:
