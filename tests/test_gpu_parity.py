@@ -128,6 +128,33 @@ def test_full_size_sampled(name):
     torch.cuda.empty_cache()
 
 
+def test_max_cache_length():
+    # the longest cache the host checks accept (2^19 rows): the selection
+    # bitmap fills the prep kernel's 64 KB of LDS, the compacted list is
+    # written straight to the workspace (the LDS staging covers up to 16384
+    # rows), the newest row sits at the top of the 32-bit row offsets, and
+    # the rotation table has 2^19 rows
+    rope = dict(W.ROPE_YARN, max_seq_len=1 << 19)
+    w = W.build("maxlen", 2, 16, [1 << 19, 20000], 512, "bf16", "bf16", rope, seed=1401)
+    dev = Dev(w)
+    out, lse, (rc, st) = dev.run(validate=True)
+    assert rc == mla.MLA_OK and st == 0
+    _check(dev, out, lse)
+    del dev
+    torch.cuda.empty_cache()
+
+
+def test_many_workgroups_and_query_chunks():
+    # 300 sequences: more attention workgroups than compute units, three
+    # 128-sequence query chunks in the absorption, ten merge batches
+    rng = np.random.default_rng(1402)
+    lens = rng.integers(1, 600, size=300)
+    w = W.build("manyseq", 300, 32, list(lens), 128, "bf16", "f32", W.ROPE_YARN, seed=1403)
+    dev = Dev(w)
+    out, lse, _ = dev.run()
+    _check(dev, out, lse)
+
+
 # ---------------------------------------------------------------------------
 # Index handling (bit-exact)
 # ---------------------------------------------------------------------------
