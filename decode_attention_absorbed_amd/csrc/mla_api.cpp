@@ -62,6 +62,7 @@ bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_split
         S = base >= num_cus ? 1 : num_cus / base;
         const int max_by_rows = (K + 2 * pl->tile_rows - 1) / (2 * pl->tile_rows);
         if (S > max_by_rows) S = max_by_rows;
+        if (S > kMaxSplits) S = kMaxSplits;
         if ((int64_t)S * H > 65536) S = 65536 / H;   // keeps 32 sequences' partials within 2 GiB
         if (S < 1) S = 1;
     }

@@ -65,6 +65,11 @@ def test_planner_and_workspace(mla):
             else:
                 assert S == 1
     assert mla.num_splits(1, 128, 1001, mla.MLA_DTYPE_BF16, 256) == 16  # >= 2 tiles of 32 rows each
+    # long selections on few sequences: the automatic plan stops at 64 splits
+    # instead of failing (B = 1..3 would otherwise ask for 85..256)
+    for B in (1, 2, 3):
+        assert mla.num_splits(B, 32, 20000, mla.MLA_DTYPE_BF16, 256) == 64
+        assert mla.workspace_size(B, 32, 20000, 1, 1, 256, 0) > 0
     assert mla.num_splits(4, 16, 65, mla.MLA_DTYPE_F32, 256) == 1
     a = mla.workspace_size(32, 128, 2048, 1, 1, 256, 0)
     b = mla.workspace_size(32, 128, 2048, 1, 1, 256, 16)

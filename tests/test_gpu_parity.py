@@ -144,6 +144,18 @@ def test_max_cache_length():
     torch.cuda.empty_cache()
 
 
+def test_long_selection():
+    # 20000 selected rows: more than the 16384-entry LDS list, hundreds of
+    # tiles per split
+    rope = dict(W.ROPE_YARN, max_seq_len=40000)
+    w = W.build("longsel", 2, 32, [40000, 30000], 20000, "bf16", "bf16", rope, seed=1404,
+                k_per_seq=[20000, 17000])
+    dev = Dev(w)
+    out, lse, (rc, st) = dev.run(validate=True)
+    assert rc == mla.MLA_OK and st == 0
+    _check(dev, out, lse)
+
+
 def test_many_workgroups_and_query_chunks():
     # 300 sequences: more attention workgroups than compute units, three
     # 128-sequence query chunks in the absorption, ten merge batches
