@@ -88,6 +88,9 @@ CASES = [
     ("h96", 2, 96, [333, 444], 150, "bf16", "bf16", "random"),
     ("f32_h128", 2, 128, [300, 129], 200, "f32", "f32", "random"),
     ("f32_h16_bf16w", 2, 16, [50, 900], 64, "f32", "bf16", "random"),
+    # more than one 128-head group per sequence, the second one partial
+    ("h160", 2, 160, [300, 700], 300, "bf16", "bf16", "random"),
+    ("h256", 1, 256, [1000], 512, "bf16", "f32", "recent"),
 ]
 
 
@@ -283,6 +286,28 @@ def test_fused_buffers_match_separate():
     wkv_b = torch.cat([dev.w_uk, dev.w_uv], dim=1).contiguous()         # [H, 256, 512]
     out1, lse1, _ = dev.run(kv=kv, pe=pe, w_uk=wkv_b[:, :128], w_uv=wkv_b[:, 128:])
     assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
+def test_strided_queries_and_output():
+    # the model's own layouts: q_nope and q_pe as views of one [B, H, 192]
+    # query tensor, and the output written into a wider [B, H, 256] buffer;
+    # same arithmetic, so the result is bit-identical to the contiguous call
+    w = W.build("strided", 3, 128, [300, 900, 50], 200, "bf16", "bf16", W.ROPE_YARN, seed=26)
+    dev = Dev(w)
+    out0, lse0, _ = dev.run()
+    q = torch.cat([dev.q_nope, dev.q_pe], dim=-1).contiguous()          # [B, H, 192]
+    wide = torch.full((w.B, w.H, 256), float("nan"), dtype=torch.float32, device="cuda")
+    out1 = wide[..., :128]
+    lse1 = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    n = mla.workspace_size(w.B, w.H, w.K, mla._dtype_code(dev.kv), mla._dtype_code(dev.w_uk), 0, 0)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    p = mla.build_params(q[..., :128], q[..., 128:], dev.w_uk, dev.w_uv, dev.kv, dev.pe, dev.idx, dev.lens,
+                         dev.rope_table, dev.scale, out1, lse1, ws)
+    assert p.q_nope_stride_h == 192 and p.out_stride_h == 256
+    mla.decode_attn(p)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+    assert torch.isnan(wide[..., 128:]).all()                            # nothing written past the rows
 
 
 def test_host_errors_launch_nothing():
