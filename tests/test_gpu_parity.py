@@ -91,6 +91,9 @@ CASES = [
     # more than one 128-head group per sequence, the second one partial
     ("h160", 2, 160, [300, 700], 300, "bf16", "bf16", "random"),
     ("h256", 1, 256, [1000], 512, "bf16", "f32", "recent"),
+    # a single head; a single cached row
+    ("h1", 3, 1, [40, 300, 1], 64, "bf16", "bf16", "random"),
+    ("f32_h1", 2, 1, [1, 77], 16, "f32", "f32", "random"),
 ]
 
 
