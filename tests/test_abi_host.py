@@ -32,7 +32,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("mla_rope_freqs", "mla_softmax_scale", "mla_decode_workspace_size", "mla_decode_attn",
-                 "mla_decode_num_splits", "mla_last_error", "mla_decode_params_size"):
+                 "mla_decode_num_splits", "mla_last_error", "mla_decode_params_size", "mla_topk",
+                 "mla_rope_apply"):
         assert want in names
 
 
@@ -198,3 +199,14 @@ def test_append_host_checks(mla, change, code):
     p = _params(mla, **{**_APPEND_OK, **change})
     rc = mla.lib().mla_decode_attn(ctypes.byref(p), None)
     assert rc == code, mla.last_error()
+
+
+@pytest.mark.parametrize("extra", [[], ["--op", "topk"]])
+def test_bench_refuses_more_than_one_gpu(extra):
+    # one GPU only: the refusal comes before any GPU work
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2", *extra],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
