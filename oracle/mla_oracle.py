@@ -34,7 +34,7 @@ Sources (the atlas pages on DeepSeek-V3.2-Exp's sparse latent attention):
                 rotary 64 per cached position; L = P + 1 keys in decode) and
                 the note that the causal mask is folded into the selection.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * YaRN correction range (the two helpers are omitted on the pages): the
     YaRN paper's correction dimension D(beta) = d ln(T0 / (2 pi beta)) /
     (2 ln base), lo = max(floor(D(beta_fast)), 0), hi = min(ceil(D(beta_slow)),
