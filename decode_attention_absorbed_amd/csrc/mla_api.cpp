@@ -63,7 +63,7 @@ bool make_plan(int B, int H, int K, int dtype_act, int num_cus, int forced_split
         const int max_by_rows = (K + 2 * pl->tile_rows - 1) / (2 * pl->tile_rows);
         if (S > max_by_rows) S = max_by_rows;
         if (S > kMaxSplits) S = kMaxSplits;
-        if ((int64_t)S * H > 65536) S = 65536 / H;   // keeps 32 sequences' partials within 2 GiB
+        if ((int64_t)S * H > 65536) S = 65536 / H;   // bounds the split partials: S * H KB per sequence
         if (S < 1) S = 1;
     }
     if (S > kMaxSplits) return false;
@@ -258,16 +258,6 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream) {
     mla::Plan plan;
     if (!make_plan(p->B, p->H, p->K, p->dtype_act, num_cus, p->num_splits, &plan))
         return fail(MLA_ERR_INVALID_ARG, "no launch plan (fp32 activations take num_splits 0 or 1)");
-    if (plan.bf16_path) {
-        // the merge kernel addresses the output, the split partials (32
-        // sequences at a time) and the split LSEs with 32-bit byte offsets
-        const int64_t osz = p->dtype_out == MLA_DTYPE_F32 ? 4 : 2;
-        const int64_t out_ext = ((int64_t)(p->B - 1) * p->out_stride_b + (int64_t)(p->H - 1) * p->out_stride_h + 128) * osz;
-        const int64_t part_ext = 31 * (int64_t)plan.splits * p->H * 1024 + 1024;
-        const int64_t lse_ext = (int64_t)p->B * plan.splits * p->H * 4;
-        if (out_ext > INT32_MAX || part_ext > INT32_MAX || lse_ext > INT32_MAX)
-            return fail(MLA_ERR_UNSUPPORTED, "output or split partials exceed the 2 GiB offset range");
-    }
     mla::Work w;
     const size_t need = mla::workspace_layout(p->B, p->H, p->K, plan.bf16_path, plan.splits, p->workspace, &w);
     if (p->workspace_size < need)

@@ -528,14 +528,19 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             *(bf16x4*)(orow + l32 * 1024 + (((4 * cb + q4) ^ l32) << 4) + 8 * g) = v;
         }
     }
-    const long long prow0 = ((long long)sc.b * a.S + sc.s) * a.H + sc.h0 + wave * 32;
-    if (g == 0 && sc.h0 + wave * 32 + l32 < a.H) a.lsepart[prow0 + l32] = l > 0.f ? ps.m_ref + log2f(l) : -INFINITY;
+    // partials are head-major, [H][B][S] rows: head h's rows for consecutive
+    // sequences are contiguous, so each merge workgroup (one head) streams
+    // one contiguous region
+    const long long hstride = (long long)a.B * a.S;
+    const long long prow0 = (long long)(sc.h0 + wave * 32) * hstride + (long long)sc.b * a.S + sc.s;
+    if (g == 0 && sc.h0 + wave * 32 + l32 < a.H)
+        a.lsepart[prow0 + l32 * hstride] = l > 0.f ? ps.m_ref + log2f(l) : -INFINITY;
     __builtin_amdgcn_s_waitcnt(0xC07F);            // this wave's LDS writes done (only it reads them)
 #pragma unroll 4
     for (int hr = 0; hr < 32; ++hr) {
         if (sc.h0 + wave * 32 + hr >= a.H) break;
         const u32x4 v = *(const u32x4*)(orow + hr * 1024 + ((lane ^ hr) << 4));
-        *(u32x4*)(a.opart + (prow0 + hr) * RANK + 8 * lane) = v;
+        *(u32x4*)(a.opart + (prow0 + hr * hstride) * RANK + 8 * lane) = v;
     }
     return false;
 }
