@@ -528,10 +528,11 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             *(bf16x4*)(orow + l32 * 1024 + (((4 * cb + q4) ^ l32) << 4) + 8 * g) = v;
         }
     }
-    // partials are head-major, [H][B][S] rows: head h's rows for consecutive
-    // sequences are contiguous, so each merge workgroup (one head) streams
-    // one contiguous region
-    const long long hstride = (long long)a.B * a.S;
+    // partials are head-major, [H][B][S] rows plus one padding row per head:
+    // head h's rows for consecutive sequences are contiguous, so each merge
+    // workgroup (one head) streams one contiguous region, and one sequence's
+    // heads are not a power of two apart
+    const long long hstride = (long long)a.B * a.S + 1;        // one padding row per head
     const long long prow0 = (long long)(sc.h0 + wave * 32) * hstride + (long long)sc.b * a.S + sc.s;
     if (g == 0 && sc.h0 + wave * 32 + l32 < a.H)
         a.lsepart[prow0 + l32 * hstride] = l > 0.f ? ps.m_ref + log2f(l) : -INFINITY;

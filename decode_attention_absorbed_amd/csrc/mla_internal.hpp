@@ -24,8 +24,8 @@ struct Work {
     int32_t* list;      // compacted selection [B][K], ascending, 1-based (position + 1)
     int32_t* counts;    // selected rows per sequence [B]
     uint32_t* status;   // validation status word
-    void* opart;        // split partials [H][B][S][512] (bf16; fp32 path: [B][H][512] fp32)
-    float* lsepart;     // [H][B][S] log2-domain sum-exp of each partial (fp32 path: [B][H])
+    void* opart;        // split partials [H][B*S+1][512] (bf16, one padding row per head; fp32 path: [B][H][512] fp32)
+    float* lsepart;     // [H][B*S+1] log2-domain sum-exp of each partial (fp32 path: [B][H])
     size_t bytes;       // total bytes used
 };
 

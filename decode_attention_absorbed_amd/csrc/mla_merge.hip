@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
         for (int t = 0; t < 2; ++t) {
             const int s = s0 + t;
             const bool ok = bA < a.B && s < a.S;
-            const long long row = ((long long)h * a.B + bA) * a.S + s;   // head-major partials
+            const long long row = (long long)h * ((long long)a.B * a.S + 1) + (long long)bA * a.S + s;   // head-major partials
             ls[t] = ok ? a.lsepart[row] : -INFINITY;
             const bf16* src = a.opart + row * RANK + col0 + 8 * g;
 #pragma unroll
