@@ -82,7 +82,7 @@ size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* b
     size_t off = 0;
     char* p = (char*)base;
     Work ww{};
-    ww.qt = p + off;       off = align256(off + (size_t)B * H * 576 * act);
+    ww.qt = p + off;       off = align256(off + (size_t)B * mla::qt_seq_stride(H) * act);
     ww.list = (int32_t*)(p + off);  off = align256(off + (size_t)B * K * 4);
     ww.counts = (int32_t*)(p + off); off = align256(off + (size_t)B * 4);
     ww.status = (uint32_t*)(p + off); off = align256(off + 4);

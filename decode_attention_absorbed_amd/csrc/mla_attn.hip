@@ -448,7 +448,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     // indices 3 and tile 1.  Q~ of this wave's 32 heads (QK^T B operand):
     // block ks holds features 16 ks + 8 (lane/32) .. +7 of head h0 + 32 wave
     // + lane%32; heads past H read as zero (outside the buffer window).
-    const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
+    const rsrc_t qsrc = make_rsrc(a.qt + sc.b * qt_seq_stride(a.H), (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
     if (nt > 0) {
 #pragma unroll
