@@ -82,17 +82,14 @@ size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* b
     size_t off = 0;
     char* p = (char*)base;
     Work ww{};
-    ww.qt = p + off;       off = align256(off + (size_t)B * mla::qt_seq_stride(H) * act);
+    ww.qt = p + off;       off = align256(off + (size_t)B * H * 576 * act);
     ww.list = (int32_t*)(p + off);  off = align256(off + (size_t)B * K * 4);
     ww.counts = (int32_t*)(p + off); off = align256(off + (size_t)B * 4);
     ww.status = (uint32_t*)(p + off); off = align256(off + 4);
     ww.opart = p + off;
-    // bf16 path: head-major rows with one padding row per head (head stride
-    // B * splits + 1 rows, so that one sequence's heads are not a power of
-    // two apart)
-    off = align256(off + (bf16_path ? ((size_t)B * splits + 1) * H * 512 * 2 : (size_t)B * H * 512 * 4));
+    off = align256(off + (bf16_path ? (size_t)B * splits * H * 512 * 2 : (size_t)B * H * 512 * 4));
     ww.lsepart = (float*)(p + off);
-    off = align256(off + (bf16_path ? ((size_t)B * splits + 1) * H * 4 : (size_t)B * H * 4));
+    off = align256(off + (size_t)B * (bf16_path ? splits : 1) * H * 4);
     ww.bytes = off;
     if (w) *w = ww;
     return off;

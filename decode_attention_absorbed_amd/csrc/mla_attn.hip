@@ -448,7 +448,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     // indices 3 and tile 1.  Q~ of this wave's 32 heads (QK^T B operand):
     // block ks holds features 16 ks + 8 (lane/32) .. +7 of head h0 + 32 wave
     // + lane%32; heads past H read as zero (outside the buffer window).
-    const rsrc_t qsrc = make_rsrc(a.qt + sc.b * qt_seq_stride(a.H), (uint32_t)a.H * ROW * 2u);
+    const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
     if (nt > 0) {
 #pragma unroll
@@ -528,11 +528,10 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             *(bf16x4*)(orow + l32 * 1024 + (((4 * cb + q4) ^ l32) << 4) + 8 * g) = v;
         }
     }
-    // partials are head-major, [H][B][S] rows plus one padding row per head:
-    // head h's rows for consecutive sequences are contiguous, so each merge
-    // workgroup (one head) streams one contiguous region, and one sequence's
-    // heads are not a power of two apart
-    const long long hstride = (long long)a.B * a.S + 1;        // one padding row per head
+    // partials are head-major, [H][B][S] rows: head h's rows for consecutive
+    // sequences are contiguous, so each merge workgroup (one head) streams
+    // one contiguous region
+    const long long hstride = (long long)a.B * a.S;
     const long long prow0 = (long long)(sc.h0 + wave * 32) * hstride + (long long)sc.b * a.S + sc.s;
     if (g == 0 && sc.h0 + wave * 32 + l32 < a.H)
         a.lsepart[prow0 + l32 * hstride] = l > 0.f ? ps.m_ref + log2f(l) : -INFINITY;

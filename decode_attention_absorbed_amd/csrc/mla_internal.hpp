@@ -20,21 +20,14 @@ struct Plan {
 
 // Carve-up of the caller's workspace.
 struct Work {
-    void* qt;           // Q~ [B][H][576] with QT_PAD elements after each sequence (bf16 or fp32)
+    void* qt;           // Q~ [B][H][576] (bf16 or fp32)
     int32_t* list;      // compacted selection [B][K], ascending, 1-based (position + 1)
     int32_t* counts;    // selected rows per sequence [B]
     uint32_t* status;   // validation status word
-    void* opart;        // split partials [H][B*S+1][512] (bf16, one padding row per head; fp32 path: [B][H][512] fp32)
-    float* lsepart;     // [H][B*S+1] log2-domain sum-exp of each partial (fp32 path: [B][H])
+    void* opart;        // split partials [H][B][S][512] (bf16; fp32 path: [B][H][512] fp32)
+    float* lsepart;     // [H][B][S] log2-domain sum-exp of each partial (fp32 path: [B][H])
     size_t bytes;       // total bytes used
 };
-
-// Q~ is [B][H][576] with QT_PAD extra elements per sequence: sequences then do
-// not start a multiple of 16 KB apart (128 heads x 1152 B is 9 x 16 KB), so
-// the workgroups that load their sequence's Q~ at the same moment do not all
-// start on the same HBM channels.
-constexpr int QT_PAD = 576;                 // one head row
-__host__ __device__ inline long long qt_seq_stride(int H) { return (long long)H * 576 + QT_PAD; }
 
 // Sizes of the workspace regions; returns the total (0 on overflow).
 size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* base, Work* w);

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
         for (int t = 0; t < 2; ++t) {
             const int s = s0 + t;
             const bool ok = bA < a.B && s < a.S;
-            const long long row = (long long)h * ((long long)a.B * a.S + 1) + (long long)bA * a.S + s;   // head-major partials
+            const long long row = ((long long)h * a.B + bA) * a.S + s;   // head-major partials
             ls[t] = ok ? a.lsepart[row] : -INFINITY;
             const bf16* src = a.opart + row * RANK + col0 + 8 * g;
 #pragma unroll
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
     __shared__ float wred[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-    const float* q = a.qt + b * qt_seq_stride(a.H) + h * ROW;
+    const float* q = a.qt + ((long long)b * a.H + h) * ROW;
     for (int i = tid; i < ROW; i += 256) qs[i] = q[i];
     __syncthreads();
     const int cnt = a.counts[b];

@@ -167,7 +167,7 @@ __device__ int block_exclusive_scan(int v, int* total, int* lds_wave) {
 template <typename QtT>
 __device__ __forceinline__ void rotate32(const PrepArgs& a, int b, int h, int f0, const float (&x)[32],
                                          const float (&t)[32]) {
-    QtT* dst = (QtT*)a.qt + b * qt_seq_stride(a.H) + h * ROW + RANK + f0;
+    QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f0;
     QtT y[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -470,7 +470,7 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
 #pragma unroll
                     for (int pp = 0; pp < NP; ++pp) acc = mfma32(bw[pp][nb][kb], aq[kb], acc);
                 if (bA < a.B) {
-                    bf16* dst = (bf16*)a.qt + bA * qt_seq_stride(a.H) + h * ROW + c0 + 32 * nb + 4 * g;
+                    bf16* dst = (bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 32 * nb + 4 * g;
 #pragma unroll
                     for (int i4 = 0; i4 < 4; ++i4) {
                         bf16x4 v;
@@ -497,7 +497,7 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
         float acc = 0.f;
 #pragma unroll
         for (int d = 0; d < D_NOPE; ++d) acc = fmaf(q[d], wc[d], acc);
-        ((float*)a.qt)[b * qt_seq_stride(a.H) + h * ROW + c] = acc;
+        ((float*)a.qt)[((long long)b * a.H + h) * ROW + c] = acc;
     }
 }
 
