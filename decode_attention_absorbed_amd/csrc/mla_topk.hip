@@ -19,14 +19,17 @@
 // largest with a block-wide scan.  The first digit spans the sign, the
 // exponent and two mantissa bits, so that keys of similar magnitude spread
 // over several bins (same-address LDS atomics within one instruction
-// serialise); the first pass also uses two histogram copies, one per half
-// of the waves.  The keys that fall in the first pass's threshold bin are
+// serialise).  The keys that fall in the first pass's threshold bin are
 // then gathered into a short LDS list (when there are at most 2048 of them),
 // so that the later passes visit only those.
-// The keys live in LDS when the row fits (up to 32768 positions), otherwise
-// every pass re-reads the row (it stays in L2).  The output pass gives each
-// wave a contiguous range of positions, visits it 64 positions at a time
-// and compacts with ballots, so the positions come out ascending.
+//
+// Two kernels share this scheme.  topk_reg_kernel (launches whose rows have
+// at most 32768 positions) keeps each thread's 16 or 32 contiguous keys in
+// registers and writes the output after one block-wide scan.  topk_kernel
+// (longer rows) keeps a row's keys in LDS when it fits and otherwise re-reads
+// the scores each pass (they stay in L2); its output pass gives each wave a
+// contiguous range of positions, visited 64 at a time and compacted with
+// ballots.  Either way the positions come out ascending.
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
 
