@@ -20,6 +20,12 @@
  *   viewed as [heads, 256, 512], W_UK = rows 0..127, W_UV = rows 128..255,
  *   latent index contiguous).
  *
+ * Beside the step: mla_topk (the selection step that produces topk_indices
+ * from per-position scores), mla_rope_apply (RoPE at per-row positions, in
+ * the interleaved or the half-split pair layout), and an optional fused
+ * append of each sequence's new cache row inside mla_decode_attn (fields
+ * kv_new / pe_new of mla_decode_params_t).
+ *
  * Conventions
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The
  *     library allocates no device memory and keeps no state between calls;
