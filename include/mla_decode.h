@@ -164,7 +164,10 @@ typedef struct mla_decode_params {
     void*  out;  int64_t out_stride_b, out_stride_h;  /* [B][H][128] in dtype_out */
     float* lse_out;            /* optional [B][H] natural-log sum-exp of the scores; may be NULL */
 
-    /* scratch: at least mla_decode_workspace_size(...) bytes, 256-byte aligned */
+    /* scratch: at least mla_decode_workspace_size(...) bytes, 256-byte aligned.
+     * Its contents are undefined between calls (nothing needs clearing); two
+     * calls whose work overlaps in time (different streams) must not share
+     * one workspace. */
     void*  workspace;  size_t workspace_size;
 
     /* optional instrumentation: NULL, or 2*MLA_NUM_KERNELS hipEvent_t handles
