@@ -280,6 +280,48 @@ def test_split_count_invariance():
         assert (lse - base_lse).abs().max().item() <= 1e-5
 
 
+def test_graph_replay_matches_eager():
+    # The throughput measurement replays the step from a HIP graph.  Every
+    # replay, with eager steps on other inputs and synchronisations between
+    # the replays, gives the eager step's outputs bit for bit; so does the
+    # step with the fused append (rewriting the same rows is idempotent).
+    w = W.build("graph", 8, 128, [3000, 64, 1500, 777, 4096, 1, 2048, 300], 1024, "bf16", "f32",
+                W.ROPE_YARN, seed=31)
+    dev = Dev(w)
+    other = Dev(W.build("graph_other", 8, 128, [900, 4000, 2, 1200, 50, 3333, 640, 2100], 1024, "bf16",
+                        "f32", W.ROPE_YARN, seed=32))
+    kv_new, pe_new = W.new_rows(w.B, "bf16", seed=33)
+    kn = torch.from_numpy(kv_new).to(torch.bfloat16).cuda()
+    pn = torch.from_numpy(pe_new).to(torch.bfloat16).cuda()
+    n = mla.workspace_size(w.B, w.H, w.K, mla._dtype_code(dev.kv), mla._dtype_code(dev.w_uk), 0, 0)
+    assert mla.num_splits(w.B, w.H, w.K, mla._dtype_code(dev.kv)) > 1
+    for append in (False, True):
+        out = torch.empty((w.B, w.H, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        extra = dict(kv_new=kn, pe_new=pn) if append else {}
+        p = mla.build_params(dev.q_nope, dev.q_pe, dev.w_uk, dev.w_uv, dev.kv, dev.pe, dev.idx, dev.lens,
+                             dev.rope_table, dev.scale, out, lse, ws, **extra)
+        mla.decode_attn(p)
+        torch.cuda.synchronize()
+        ref_out, ref_lse = out.clone(), lse.clone()
+        if not append:
+            _check(dev, out, lse, batch=[0, 3, 5, 7])
+        stream = torch.cuda.Stream()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            mla.decode_attn(p)
+        for r in range(4):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            ws.fill_(0xFF)
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), (append, r)
+            other.run()                     # an eager step on other inputs (synchronises)
+        del graph
+
+
 def test_fused_buffers_match_separate():
     w = W.build("fused", 3, 128, [300, 900, 50], 200, "bf16", "bf16", W.ROPE_YARN, seed=25)
     dev = Dev(w)
