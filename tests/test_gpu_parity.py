@@ -106,6 +106,62 @@ def test_small_cases(case):
     _check(dev, out, lse)
 
 
+def _sweep_cases(n=24, seed=2024):
+    """Seeded random configurations: head counts around the 32-head wave and
+    128-head workgroup boundaries, ragged lengths down to a single row, K not
+    a multiple of the 32-row tile, both dtypes, forced split counts, and rows
+    with -1 slots and duplicates in random places."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        B = int(rng.integers(1, 7))
+        H = int(rng.choice([1, 2, 16, 31, 33, 64, 100, 128, 129, 200]))
+        lens = [int(x) for x in rng.integers(1, 2200, size=B)]
+        if rng.random() < 0.3:
+            lens[int(rng.integers(B))] = 1
+        K = int(rng.integers(1, 400))
+        da = "f32" if rng.random() < 0.25 else "bf16"
+        dw = "f32" if rng.random() < 0.5 else "bf16"
+        sel = str(rng.choice(["random", "recent", "alternate"]))
+        splits = int(rng.choice([0, 1])) if da == "f32" else int(rng.choice([0, 0, 1, 2, 3, 7]))
+        cases.append((f"sweep{i}", B, H, lens, K, da, dw, sel, splits, bool(rng.random() < 0.5),
+                      int(rng.integers(1 << 30))))
+    return cases
+
+
+def _scramble(w, seed):
+    """Move -1 slots to random places and fill some of them (or some taken
+    slots) with duplicates of selected positions; every row keeps at least
+    one position."""
+    rng = np.random.default_rng(seed)
+    for b in range(w.B):
+        row = w.topk_indices[b]
+        valid = row[row >= 0]
+        holes = np.flatnonzero(row < 0)
+        if len(holes) == 0 and len(row) > 1:
+            holes = rng.choice(len(row), size=max(1, len(row) // 8), replace=False)
+            keep = np.setdiff1d(np.arange(len(row)), holes)
+            valid = row[keep]
+            row[holes] = -1
+        dup = holes[: len(holes) // 2]
+        row[dup] = rng.choice(valid, size=len(dup))
+        w.topk_indices[b] = rng.permutation(row)
+        assert (w.topk_indices[b] >= 0).any()
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: c[0])
+def test_random_configurations(case):
+    name, B, H, lens, K, da, dw, sel, splits, scramble, seed = case
+    w = W.build(name, B, H, lens, K, da, dw, W.ROPE_YARN, seed=seed, selection=sel)
+    if scramble:
+        _scramble(w, seed + 1)
+    print(f"[{name}] B={B} H={H} K={K} lens={lens} {da}/{dw} {sel} splits={splits} scrambled={scramble}",
+          flush=True)
+    dev = Dev(w)
+    out, lse, _ = dev.run(num_splits=splits)
+    _check(dev, out, lse)
+
+
 def test_bf16_output():
     w = W.build("bf16out", 3, 128, [400, 50, 999], 256, "bf16", "bf16", W.ROPE_YARN, seed=11)
     dev = Dev(w)
