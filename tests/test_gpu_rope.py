@@ -122,3 +122,46 @@ def test_rope_apply_position_out_of_table_gives_nan():
     assert torch.isfinite(y[0]).all() and torch.isfinite(y[3]).all()
     ref = _reference(x.cpu().numpy().astype(np.float64)[[0, 3]], [5, 16383], False)
     assert _rel_l2(y[[0, 3]].numpy(), ref) <= 1e-5
+
+
+def _rope_sweep(n=16, seed=1300):
+    """Seeded random shapes: row and vector strides padded by multiples of 8
+    elements, both dtypes and layouts, in place or into a separate tensor."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        cases.append((f"sweep{i}", int(rng.integers(1, 3000)), int(rng.choice([1, 3, 16, 64, 128])),
+                      str(rng.choice(["bf16", "f32"])), bool(rng.random() < 0.5), int(rng.integers(0, 3)),
+                      int(rng.integers(0, 3)), bool(rng.random() < 0.5), int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _rope_sweep(), ids=lambda c: c[0])
+def test_rope_apply_random_shapes(case):
+    name, N, H, dtype, interleaved, pad_h, pad_n, in_place, seed = case
+    rng = np.random.default_rng(seed)
+    T = W.ROPE_YARN["max_seq_len"]
+    sh = 64 + 8 * pad_h
+    sn = (H - 1) * sh + 64 + 8 * pad_n
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    buf = torch.from_numpy(rng.standard_normal(N * sn).astype(np.float32)).to(td).cuda()
+    before = buf.clone()
+    x = buf.as_strided((N, H, 64), (sn, sh, 1))
+    pos = rng.integers(0, T, size=N).astype(np.int32)
+    pos[0] = 0
+    pos[-1] = T - 1
+    pd = torch.from_numpy(pos).cuda()
+    print(f"[rope {name}] N={N} H={H} {dtype} interleaved={interleaved} strides ({sn}, {sh}) "
+          f"in_place={in_place}", flush=True)
+    x64 = x.float().cpu().numpy().astype(np.float64)
+    y = mla.rope_apply(x, pd, _table(), interleaved, out=x if in_place else None)
+    torch.cuda.synchronize()
+    ref = _reference(x64, pos, interleaved)
+    bar = 1e-2 if dtype == "bf16" else 1e-5
+    assert _rel_l2(y.float().cpu().numpy(), ref) <= bar
+    # the elements between the vectors are never written
+    mask = torch.ones(N * sn, dtype=torch.bool)
+    mask.as_strided((N, H, 64), (sn, sh, 1)).fill_(False)
+    assert torch.equal(buf.cpu()[mask], before.cpu()[mask])
+    if not in_place:
+        assert torch.equal(buf.cpu(), before.cpu())

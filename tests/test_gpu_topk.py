@@ -139,3 +139,42 @@ def test_topk_feeds_decode():
     err = rel_l2_rows(out.float().cpu().numpy(), ref).max()
     print(f"[topk feed] max rel L2 {err:.3e}", flush=True)
     assert err <= 1e-2
+
+
+def _topk_sweep(n=20, seed=1200):
+    """Seeded random shapes over all three kernel forms (rows up to 16384 and
+    up to 32768 keys in registers, longer rows re-read), k from 1 to past the
+    row length, and score mixes: normal, heavy ties, a narrow band of nearby
+    floats, magnitudes from denormals to 1e38, with NaN / -0 / +-inf mixed in."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        L = int(rng.choice([1, 37, 2048, 9000, 16384, 16385, 25000, 32768, 40000]))
+        B = int(rng.integers(1, 9))
+        k = int(rng.choice([1, 2, 100, 1024, 2048, 3000]))
+        kind = str(rng.choice(["normal", "ties", "band", "wide"]))
+        cases.append((f"sweep{i}", B, L, k, kind, bool(rng.random() < 0.5), int(rng.integers(1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _topk_sweep(), ids=lambda c: c[0])
+def test_topk_random_shapes(case):
+    name, B, L, k, kind, specials, seed = case
+    rng = np.random.default_rng(seed)
+    if kind == "normal":
+        scores = rng.standard_normal((B, L)).astype(np.float32)
+    elif kind == "ties":
+        scores = rng.integers(-4, 5, size=(B, L)).astype(np.float32)
+    elif kind == "band":
+        # consecutive floats around 1.0: keys differ only in their low bits
+        scores = (np.float32(1.0) + rng.integers(-300, 300, size=(B, L)).astype(np.float32)
+                  * np.float32(2.0 ** -23)).astype(np.float32)
+    else:
+        mag = 10.0 ** rng.uniform(-44, 38, size=(B, L))
+        scores = (np.sign(rng.standard_normal((B, L))) * mag).astype(np.float32)
+    if specials:
+        for v, p in ((np.nan, 0.03), (-0.0, 0.05), (0.0, 0.02), (np.inf, 0.005), (-np.inf, 0.01)):
+            scores[rng.random((B, L)) < p] = v
+    lens = rng.integers(0, L + 1, size=B)
+    lens[0] = L
+    _check(scores, lens, k, f"{name} {kind}{' +specials' if specials else ''}")
