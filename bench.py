@@ -362,7 +362,12 @@ def main():
     torch.cuda.synchronize()
 
     # Per-kernel durations: K eager steps with HIP events recorded by the
-    # library around each of its kernels on the launch stream.
+    # library around each of its kernels on the launch stream.  They follow
+    # 50 more untimed steps: for the first ~3 ms of steady load the clock is
+    # still rising (launches run ~8% slower), and the kernel averages are
+    # meant to describe the steady state.
+    for i in range(50):
+        mla.decode_attn(plain[i % R])
     for i in range(K):
         mla.decode_attn(timed[i])
     torch.cuda.synchronize()
