@@ -182,24 +182,80 @@ def _inner_contig(name, t, width):
         raise ValueError(f"{name}: last dimension must be {width} and contiguous")
 
 
+def _on_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device.type != "cuda":
+            raise ValueError(f"{name} must be a GPU tensor (the library takes device pointers)")
+
+
+def _rope_table_ok(rope_table):
+    torch = _torch()
+    if rope_table.dtype != torch.float32 or rope_table.dim() != 3 or tuple(rope_table.shape[1:]) != (32, 2) \
+            or not rope_table.is_contiguous():
+        raise ValueError("rope_table must be a contiguous float32 [T, 32, 2] table from rope_freqs")
+
+
+def _check_decode_tensors(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
+                          out, lse):
+    """Shapes, dtypes and layouts the header requires of the decode step's
+    tensors; raises before anything is passed to the library."""
+    torch = _torch()
+    dims = (("q_nope", q_nope, 3), ("q_pe", q_pe, 3), ("w_uk", w_uk, 3), ("w_uv", w_uv, 3),
+            ("kv_cache", kv_cache, 3), ("pe_cache", pe_cache, 3), ("topk_indices", topk_indices, 2),
+            ("cache_lens", cache_lens, 1), ("out", out, 3))
+    for name, t, d in dims:
+        if t.dim() != d:
+            raise ValueError(f"{name} must have {d} dimensions, got shape {tuple(t.shape)}")
+    B, H = q_nope.shape[0], q_nope.shape[1]
+    for name, t, w in (("q_nope", q_nope, 128), ("q_pe", q_pe, 64), ("w_uk", w_uk, 512), ("w_uv", w_uv, 512),
+                       ("kv_cache", kv_cache, 512), ("pe_cache", pe_cache, 64), ("out", out, 128)):
+        _inner_contig(name, t, w)
+    # one activation dtype for the queries and both caches (dtype_act)
+    act = kv_cache.dtype
+    if act not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"kv_cache must be bfloat16 or float32, got {act}")
+    for name, t in (("q_nope", q_nope), ("q_pe", q_pe), ("pe_cache", pe_cache)):
+        if t.dtype != act:
+            raise TypeError(f"{name} is {t.dtype} but kv_cache is {act}: queries and caches share one dtype")
+    if w_uk.dtype not in (torch.bfloat16, torch.float32) or w_uv.dtype != w_uk.dtype:
+        raise TypeError("w_uk and w_uv must both be bfloat16 or both float32")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bfloat16 or float32")
+    # leading dimensions: B sequences, H heads
+    if tuple(q_pe.shape[:2]) != (B, H):
+        raise ValueError(f"q_pe must be [{B}, {H}, 64] like q_nope, got {tuple(q_pe.shape)}")
+    for name, t in (("w_uk", w_uk), ("w_uv", w_uv)):
+        if t.shape[0] < H or t.shape[1] != 128 or t.stride(1) != 512:
+            raise ValueError(f"{name} must be [H={H}, 128, 512] with contiguous rows, got {tuple(t.shape)}")
+    if kv_cache.shape[0] < B or pe_cache.shape[0] < B:
+        raise ValueError(f"kv_cache / pe_cache must hold B={B} sequences")
+    if pe_cache.shape[1] < kv_cache.shape[1]:
+        raise ValueError("pe_cache must have as many rows per sequence as kv_cache")
+    if topk_indices.dtype != torch.int32 or cache_lens.dtype != torch.int32:
+        raise TypeError("topk_indices and cache_lens must be int32")
+    if topk_indices.shape[0] < B or topk_indices.stride(1) != 1:
+        raise ValueError(f"topk_indices must be [B={B}, K] with contiguous rows")
+    if cache_lens.shape[0] < B or cache_lens.stride(0) != 1:
+        raise ValueError(f"cache_lens must be a contiguous int32 [B={B}]")
+    if out.shape[0] < B or out.shape[1] < H:
+        raise ValueError(f"out must be [B={B}, H={H}, 128], got {tuple(out.shape)}")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 [B={B}, H={H}] tensor")
+    _rope_table_ok(rope_table)
+
+
 def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
                  softmax_scale, out, lse=None, workspace=None, num_splits=0, num_cus=0, validate=False,
                  events=None, kv_new=None, pe_new=None) -> DecodeParams:
     """Fill mla_decode_params_t from torch tensors (shapes as in the header).
     kv_new [B, 512] and pe_new [B, 64] (both or neither) switch on the fused
-    append of each sequence's row p_b = L_b - 1 into kv_cache / pe_cache."""
-    torch = _torch()
+    append of each sequence's row p_b = L_b - 1 into kv_cache / pe_cache.
+    Every tensor must live on the GPU; shapes, dtypes and layouts are checked
+    first (ValueError / TypeError)."""
+    _check_decode_tensors(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cache_lens, rope_table,
+                          out, lse)
     B, H = q_nope.shape[0], q_nope.shape[1]
     K = topk_indices.shape[1]
-    for name, t, w in (("q_nope", q_nope, 128), ("q_pe", q_pe, 64), ("w_uk", w_uk, 512), ("w_uv", w_uv, 512),
-                       ("kv_cache", kv_cache, 512), ("pe_cache", pe_cache, 64), ("out", out, 128)):
-        _inner_contig(name, t, w)
-    if w_uk.stride(1) != 512 or w_uv.stride(1) != 512:
-        raise ValueError("w_uk / w_uv rows must be contiguous [H, 128, 512]")
-    if topk_indices.dtype != torch.int32 or cache_lens.dtype != torch.int32:
-        raise TypeError("topk_indices and cache_lens must be int32")
-    if topk_indices.stride(1) != 1:
-        raise ValueError("topk_indices rows must be contiguous")
     p = DecodeParams()
     p.B, p.H, p.K = B, H, K
     p.d_nope, p.d_rope, p.d_v, p.kv_rank = 128, 64, 128, 512
@@ -233,8 +289,15 @@ def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cac
         _inner_contig("pe_new", pe_new, 64)
         if kv_new.dtype != kv_cache.dtype or pe_new.dtype != kv_cache.dtype:
             raise TypeError("kv_new / pe_new must have the caches' dtype")
+        if kv_new.dim() != 2 or pe_new.dim() != 2 or kv_new.shape[0] < B or pe_new.shape[0] < B:
+            raise ValueError(f"kv_new / pe_new must be [B={B}, 512] / [B={B}, 64]")
         p.kv_new, p.kv_new_stride_b = kv_new.data_ptr(), kv_new.stride(0)
         p.pe_new, p.pe_new_stride_b = pe_new.data_ptr(), pe_new.stride(0)
+    if workspace is not None and workspace.dtype != _torch().uint8:
+        raise TypeError("workspace must be a uint8 tensor")
+    _on_gpu(q_nope=q_nope, q_pe=q_pe, w_uk=w_uk, w_uv=w_uv, kv_cache=kv_cache, pe_cache=pe_cache,
+            topk_indices=topk_indices, cache_lens=cache_lens, rope_table=rope_table, out=out, lse=lse,
+            workspace=workspace, kv_new=kv_new, pe_new=pe_new)
     return p
 
 
@@ -274,11 +337,22 @@ def topk(scores, cache_lens, k, out=None, stream=None):
     scores per row (-1 padded).  scores: float32 [B, L] (inner dim contiguous),
     cache_lens: int32 [B]; all on the device."""
     torch = _torch()
+    if scores.dim() != 2:
+        raise MLAError(MLA_ERR_INVALID_ARG, "scores must be [B, L]")
     B, L = scores.shape
     if scores.dtype != torch.float32 or scores.stride(1) != 1:
         raise MLAError(MLA_ERR_INVALID_ARG, "scores must be float32 with a contiguous inner dimension")
+    if cache_lens.dtype != torch.int32 or cache_lens.dim() != 1 or cache_lens.shape[0] < B \
+            or cache_lens.stride(0) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"cache_lens must be a contiguous int32 [B={B}]")
     if out is None:
         out = torch.empty((B, k), dtype=torch.int32, device=scores.device)
+    if out.dtype != torch.int32 or out.dim() != 2 or out.shape[0] < B or out.shape[1] < k or out.stride(1) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"out must be int32 [B={B}, >={k}] with contiguous rows")
+    try:
+        _on_gpu(scores=scores, cache_lens=cache_lens, out=out)
+    except ValueError as e:
+        raise MLAError(MLA_ERR_INVALID_ARG, str(e))
     p = TopkParams()
     p.B, p.k, p.max_len, p.reserved = B, k, L, 0
     p.scores, p.score_stride = scores.data_ptr(), scores.stride(0)
@@ -306,10 +380,21 @@ def rope_apply(x, positions, rope_table, interleaved, out=None, stream=None):
         dt = MLA_DTYPE_F32
     else:
         raise MLAError(MLA_ERR_INVALID_ARG, "x must be bfloat16 or float32")
+    if positions.dtype != torch.int32 or positions.dim() != 1 or positions.shape[0] < xv.shape[0] \
+            or positions.stride(0) != 1:
+        raise MLAError(MLA_ERR_INVALID_ARG, f"positions must be a contiguous int32 [N={xv.shape[0]}]")
+    try:
+        _rope_table_ok(rope_table)
+    except ValueError as e:
+        raise MLAError(MLA_ERR_INVALID_ARG, str(e))
     if out is None:
         out = torch.empty_like(x, memory_format=torch.contiguous_format)
     if out.shape != x.shape or out.dtype != x.dtype:
         raise MLAError(MLA_ERR_INVALID_ARG, "out must match x in shape and dtype")
+    try:
+        _on_gpu(x=x, positions=positions, rope_table=rope_table, out=out)
+    except ValueError as e:
+        raise MLAError(MLA_ERR_INVALID_ARG, str(e))
     yv = out.unsqueeze(1) if squeeze else out
     p = RopeApplyParams()
     p.N, p.H = xv.shape[0], xv.shape[1]

@@ -162,7 +162,8 @@ typedef struct mla_decode_params {
 
     /* outputs */
     void*  out;  int64_t out_stride_b, out_stride_h;  /* [B][H][128] in dtype_out */
-    float* lse_out;            /* optional [B][H] natural-log sum-exp of the scores; may be NULL */
+    float* lse_out;            /* optional contiguous [B][H] float32 (element b*H + h): natural-log
+                                * sum-exp of the scores; may be NULL */
 
     /* scratch: at least mla_decode_workspace_size(...) bytes, 256-byte aligned.
      * Its contents are undefined between calls (nothing needs clearing); two

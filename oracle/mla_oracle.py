@@ -106,10 +106,12 @@ def inv_freq(cfg: RopeConfig) -> np.ndarray:
     lo, hi = float(lo), float(hi)
     if hi == lo:
         hi += 0.001
-    ramp = np.clip((i - lo) / (hi - lo), 0.0, 1.0)
-    smooth = 1.0 - ramp
-    # [rope]: freqs / factor * (1 - smooth) + freqs * smooth
-    return theta / cfg.factor * (1.0 - smooth) + theta * smooth
+    # gamma_i: 0 below lo (pairs that keep their frequency), 1 above hi
+    # (pairs slowed by the factor), linear in between
+    gamma = np.clip((i - lo) / (hi - lo), 0.0, 1.0)
+    # [rope] (page "Transformer blocks / RoPE coefficients"): each frequency
+    # is a gamma-weighted mix of theta_i / factor and theta_i
+    return theta / cfg.factor * gamma + theta * (1.0 - gamma)
 
 
 def rope_cos_sin(positions, cfg: RopeConfig) -> np.ndarray:

@@ -210,3 +210,77 @@ def test_bench_refuses_more_than_one_gpu(extra):
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+# ---------------------------------------------------------------------------
+# The binding's own checks (mla.build_params / topk / rope_apply): wrong
+# dtypes, layouts and leading dimensions raise before any pointer reaches the
+# library.  CPU tensors serve as stand-ins; the last check rejects them.
+# ---------------------------------------------------------------------------
+def _decode_tensors(B=2, H=4, L=16, K=8, act="bf16", wdt="f32"):
+    import torch
+    a = torch.bfloat16 if act == "bf16" else torch.float32
+    w = torch.bfloat16 if wdt == "bf16" else torch.float32
+    return dict(q_nope=torch.zeros(B, H, 128, dtype=a), q_pe=torch.zeros(B, H, 64, dtype=a),
+                w_uk=torch.zeros(H, 128, 512, dtype=w), w_uv=torch.zeros(H, 128, 512, dtype=w),
+                kv_cache=torch.zeros(B, L, 512, dtype=a), pe_cache=torch.zeros(B, L, 64, dtype=a),
+                topk_indices=torch.zeros(B, K, dtype=torch.int32), cache_lens=torch.full((B,), L, dtype=torch.int32),
+                rope_table=torch.zeros(64, 32, 2), softmax_scale=0.1, out=torch.zeros(B, H, 128),
+                lse=torch.zeros(B, H))
+
+
+def _bad_decode_cases():
+    import torch
+    return [
+        ("q_pe_dtype", dict(q_pe=torch.zeros(2, 4, 64)), TypeError),            # fp32 q_pe, bf16 caches
+        ("q_nope_dtype", dict(q_nope=torch.zeros(2, 4, 128)), TypeError),
+        ("pe_cache_dtype", dict(pe_cache=torch.zeros(2, 16, 64)), TypeError),
+        ("w_mixed", dict(w_uv=torch.zeros(4, 128, 512, dtype=torch.bfloat16)), TypeError),
+        ("lse_dtype", dict(lse=torch.zeros(2, 4, dtype=torch.float64)), ValueError),
+        ("lse_strided", dict(lse=torch.zeros(4, 2).t()), ValueError),
+        ("lse_shape", dict(lse=torch.zeros(2, 3)), ValueError),
+        ("out_short_b", dict(out=torch.zeros(1, 4, 128)), ValueError),
+        ("out_short_h", dict(out=torch.zeros(2, 3, 128)), ValueError),
+        ("idx_short_b", dict(topk_indices=torch.zeros(1, 8, dtype=torch.int32)), ValueError),
+        ("idx_dtype", dict(topk_indices=torch.zeros(2, 8, dtype=torch.int64)), TypeError),
+        ("lens_short", dict(cache_lens=torch.zeros(1, dtype=torch.int32)), ValueError),
+        ("lens_dtype", dict(cache_lens=torch.zeros(2, dtype=torch.int64)), TypeError),
+        ("kv_short_b", dict(kv_cache=torch.zeros(1, 16, 512, dtype=torch.bfloat16)), ValueError),
+        ("pe_short_rows", dict(pe_cache=torch.zeros(2, 8, 64, dtype=torch.bfloat16)), ValueError),
+        ("w_short_h", dict(w_uk=torch.zeros(3, 128, 512)), ValueError),
+        ("q_pe_shape", dict(q_pe=torch.zeros(2, 3, 64, dtype=torch.bfloat16)), ValueError),
+        ("table_dtype", dict(rope_table=torch.zeros(64, 32, 2, dtype=torch.float64)), ValueError),
+        ("table_shape", dict(rope_table=torch.zeros(64, 64)), ValueError),
+        ("act_f16", dict(kv_cache=torch.zeros(2, 16, 512, dtype=torch.float16)), TypeError),
+        ("cpu_tensors", dict(), ValueError),                                     # all valid, but on the host
+    ]
+
+
+@pytest.mark.parametrize("case", range(21))
+def test_binding_rejects_bad_decode_tensors(case):
+    pytest.importorskip("torch")
+    from decode_attention_absorbed_amd import mla as m
+    name, change, exc = _bad_decode_cases()[case]
+    t = {**_decode_tensors(), **change}
+    with pytest.raises(exc):
+        m.build_params(**t)
+
+
+def test_binding_rejects_bad_topk_and_rope_tensors():
+    torch = pytest.importorskip("torch")
+    from decode_attention_absorbed_amd import mla as m
+    scores = torch.zeros(4, 100)
+    with pytest.raises(m.MLAError):
+        m.topk(scores, torch.zeros(4, dtype=torch.int64), 8)                   # int64 lengths
+    with pytest.raises(m.MLAError):
+        m.topk(scores, torch.zeros(3, dtype=torch.int32), 8)                   # too few lengths
+    with pytest.raises(m.MLAError):
+        m.topk(scores, torch.zeros(4, dtype=torch.int32), 8)                   # host tensors
+    x = torch.zeros(8, 4, 64, dtype=torch.bfloat16)
+    table = torch.zeros(16, 32, 2)
+    with pytest.raises(m.MLAError):
+        m.rope_apply(x, torch.zeros(8, dtype=torch.int64), table, True)        # int64 positions
+    with pytest.raises(m.MLAError):
+        m.rope_apply(x, torch.zeros(8, dtype=torch.int32), table.double(), True)
+    with pytest.raises(m.MLAError):
+        m.rope_apply(x, torch.zeros(8, dtype=torch.int32), table, True)        # host tensors
