@@ -83,6 +83,7 @@ size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* b
     char* p = (char*)base;
     Work ww{};
     ww.qt = p + off;       off = align256(off + (size_t)B * H * 576 * act);
+    ww.qlo = p + off;      off = align256(off + (bf16_path ? (size_t)B * H * 64 * 2 : 0));
     ww.list = (int32_t*)(p + off);  off = align256(off + (size_t)B * K * 4);
     ww.counts = (int32_t*)(p + off); off = align256(off + (size_t)B * 4);
     ww.status = (uint32_t*)(p + off); off = align256(off + 4);

@@ -42,6 +42,7 @@ struct AttnArgs {
     int B, H, K, S, HG;
     float scale_log2;
     const bf16* qt;
+    const bf16* qlo;           // low bf16 parts of the rotary queries: [B][H][64]
     const int32_t* list;
     const int32_t* counts;
     const bf16* kv; long long kv_sb, kv_st;
@@ -289,9 +290,25 @@ __device__ __forceinline__ void soft2(const f32x16& acc, int i, float m_ref, flo
 // tile (its first reads are issued during steps 3..7).
 constexpr int RING = 4;
 constexpr int PV_AHEAD = RING - 1;
-constexpr int QK_AHEAD = 5;
-constexpr int NSTEP = 68;
+constexpr int QK_AHEAD = 3;
+// The QK^T chain: the 32 latent feature blocks, then each of the 4 rotary
+// blocks twice, against the high and then the low bf16 part of the rotary
+// query (q^ = hi + lo to 16 significant bits: its rounding to bf16 would
+// otherwise move every score by up to 2^-9 of the rotary term).
+constexpr int NLO = 4;
+constexpr int NQK = ROW / 16 + NLO;                  // 40 MFMAs
+constexpr int QK_END = 8 + NQK;                      // first step after the chain
+constexpr int NSTEP = 32 + NQK;                      // 72
 static_assert(32 % RING == 0, "ring alignment");
+// Chain step j: feature block and whether it takes the low rotary part.
+__host__ __device__ constexpr int chain_block(int j) { return j < 32 ? j : 32 + (j - 32) / 2; }
+__host__ __device__ constexpr bool chain_lo(int j) { return j >= 32 && ((j - 32) & 1) != 0; }
+// K operands of the chain live in a ring of QK_AHEAD + 1 slots indexed by
+// block: block j + QK_AHEAD is loaded while block j is in use, and the
+// rotary blocks, used twice, are loaded QK_AHEAD chain steps before their
+// first use, when the block four before them is already dead.
+constexpr int KRING = QK_AHEAD + 1;
+static_assert(KRING == 4, "the rotary blocks' reuse is checked for a ring of 4");
 
 // A operand of PV step (kt, cb) of the tile in stage st.
 __device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0, int t1, int kt, int cb) {
@@ -311,8 +328,9 @@ __device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0
 template <typename Hook>
 __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const char* __restrict__ prv,
                                           const char* __restrict__ smem_q, const LaneOffsets& lo,
-                                          const bf16x8 (&qreg)[QK_REG], PassState& ps, bf16x8 (&ring)[RING],
-                                          bf16x8& ptail, float scale_log2, int rem, bool first, Hook&& hook) {
+                                          const bf16x8 (&qreg)[QK_REG], const bf16x8 (&qlo)[NLO], PassState& ps,
+                                          bf16x8 (&ring)[RING], bf16x8& ptail, float scale_log2, int rem, bool first,
+                                          Hook&& hook) {
     int qb = lo.qk, rb = lo.rot, t0 = lo.tr[0], t1 = lo.tr[1], qo = lo.q;
     opaque(qb);
     opaque(rb);
@@ -329,32 +347,37 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
         const int addr = ks < 32 ? qb + 32 * ks : (ks == 32 ? rb : rb ^ ((ks - 32) << 5));
         return *(const bf16x8*)(cur + addr);
     };
-    bf16x8 kv[QK_AHEAD + 1];
+    bf16x8 kv[KRING];
     bf16x8 qv[QK_LDS];
     f32x16 acc;
     bf16x8 p0 = {}, p1 = {};
 #pragma clang loop unroll(full)
     for (int s = 0; s < NSTEP; ++s) {
-        const bool is_qk = s >= 8 && s < 44;
-        const int pvs = s < 8 ? s : s - 36;                             // PV step index (PV steps only)
+        const bool is_qk = s >= 8 && s < QK_END;
+        const int pvs = s < 8 ? s : s - NQK;                            // PV step index (PV steps only)
         if (!is_qk) ring[(pvs + PV_AHEAD) % RING] = pv_load(pvs + PV_AHEAD);
-        if (s >= 8 - QK_AHEAD && s < 44 - QK_AHEAD) {
-            const int kl = s - (8 - QK_AHEAD);
-            kv[kl % (QK_AHEAD + 1)] = qk_load(kl);
-            if (kl >= QK_REG) qv[kl - QK_REG] = *(const bf16x8*)(smem_q + qo + 4096 * (kl - QK_REG));
+        {
+            // operand of chain step jl, read QK_AHEAD steps ahead (once per block)
+            const int jl = s - 8 + QK_AHEAD;
+            if (jl >= 0 && jl < NQK && !chain_lo(jl)) {
+                const int kl = chain_block(jl);
+                kv[kl % KRING] = qk_load(kl);
+                if (kl >= QK_REG) qv[kl - QK_REG] = *(const bf16x8*)(smem_q + qo + 4096 * (kl - QK_REG));
+            }
         }
         if (!is_qk) {
             const bf16x8 av = ring[pvs % RING];
             const int cb = pvs & 15;
             ps.o[cb] = mfma32(av, pvs < 16 ? ptail : p0, ps.o[cb]);
         } else {
-            const int ks = s - 8;
-            const bf16x8 q = ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks >= QK_REG ? ks - QK_REG : 0];
-            const bf16x8 k = kv[ks % (QK_AHEAD + 1)];
-            if (ks == 0) qk_mfma_first(acc, k, q);
+            const int j = s - 8, ks = chain_block(j);
+            const bf16x8 q = chain_lo(j) ? qlo[ks - 32 >= 0 ? ks - 32 : 0]
+                                         : (ks < QK_REG ? qreg[ks < QK_REG ? ks : 0] : qv[ks >= QK_REG ? ks - QK_REG : 0]);
+            const bf16x8 k = kv[ks % KRING];
+            if (j == 0) qk_mfma_first(acc, k, q);
             else qk_mfma(acc, k, q);
         }
-        if (s == 43) {
+        if (s == QK_END - 1) {
             qk_settle(acc);
             if (rem < R) {
                 // last tile, partly filled: rows past the end score -inf
@@ -375,9 +398,10 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
                 ps.m_ref = floorf(mt);
             }
         }
-        if (s >= 44 && s < 48) soft2(acc, 2 * (s - 44), ps.m_ref, scale_log2, ps.lsum, p0, 2 * (s - 44));
-        if (s == 49) ps.mraw = max17_raw(ps.mraw, acc);
-        if (s >= 53 && s < 57) soft2(acc, 8 + 2 * (s - 53), ps.m_ref, scale_log2, ps.lsum, p1, 2 * (s - 53));
+        constexpr int S0 = QK_END, S1 = QK_END + 9;       // softmax of rows 0..15, then 16..31
+        if (s >= S0 && s < S0 + 4) soft2(acc, 2 * (s - S0), ps.m_ref, scale_log2, ps.lsum, p0, 2 * (s - S0));
+        if (s == S0 + 5) ps.mraw = max17_raw(ps.mraw, acc);
+        if (s >= S1 && s < S1 + 4) soft2(acc, 8 + 2 * (s - S1), ps.m_ref, scale_log2, ps.lsum, p1, 2 * (s - S1));
         hook(s);
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -450,6 +474,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     // + lane%32; heads past H read as zero (outside the buffer window).
     const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
+    bf16x8 qlo[NLO];
     if (nt > 0) {
 #pragma unroll
         for (int T = 0; T < 2; ++T) fetch_idx(sc, T, slot(T));
@@ -466,8 +491,14 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             for (int ks = 0; ks < QK_REG; ++ks)
                 qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                                           qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
+            // low parts of the rotary query: [H][64] per sequence
+            const rsrc_t lsrc = make_rsrc(a.qlo + (long long)sc.b * a.H * D_ROPE, (uint32_t)a.H * D_ROPE * 2u);
+#pragma unroll
+            for (int i = 0; i < NLO; ++i)
+                qlo[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        lsrc, h * (D_ROPE * 2) + (16 * i + 8 * g) * 2, 0, 0));
         }
-        wait_vmcnt<QK_LDS + QK_REG>();             // the two index fetches (issued first) landed
+        wait_vmcnt<QK_LDS + QK_REG + NLO>();       // the two index fetches (issued first) landed
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
             fetch_idx(sc, T + 2, slot(T + 2));
@@ -493,7 +524,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
         const TileRows rows = read_rows(slot(it + 2));
         MLA_LDS char* const dst = lstage(it + 2);
         int* const fslot = slot(it + 4);
-        tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, ps, ring, ptail, a.scale_log2,
+        tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, qlo, ps, ring, ptail, a.scale_log2,
                   nrows - it * R, it == 0 && !known, [&](int st_) {
             // copies of tile it+2 spread over the tile's 68 MFMA steps
             if (st_ == 1) fetch_idx(sc, it + 4, fslot);
@@ -606,7 +637,7 @@ hipError_t launch_attn(const mla_decode_params_t& p, const Plan& plan, const Wor
     AttnArgs a{};
     a.B = p.B; a.H = p.H; a.K = p.K; a.S = plan.splits; a.HG = plan.hgroups;
     a.scale_log2 = p.softmax_scale * LOG2E;
-    a.qt = (const bf16*)w.qt; a.list = w.list; a.counts = w.counts;
+    a.qt = (const bf16*)w.qt; a.qlo = (const bf16*)w.qlo; a.list = w.list; a.counts = w.counts;
     a.kv = (const bf16*)p.kv_cache; a.kv_sb = p.kv_stride_b; a.kv_st = p.kv_stride_t;
     a.pe = (const bf16*)p.pe_cache; a.pe_sb = p.pe_stride_b; a.pe_st = p.pe_stride_t;
     a.kv_win = (uint32_t)((long long)(p.max_cache_len - 1) * p.kv_stride_t * 2 + RANK * 2);

@@ -21,6 +21,7 @@ struct Plan {
 // Carve-up of the caller's workspace.
 struct Work {
     void* qt;           // Q~ [B][H][576] (bf16 or fp32)
+    void* qlo;          // bf16 path: low bf16 parts of Q~'s rotary features [B][H][64]
     int32_t* list;      // compacted selection [B][K], ascending, 1-based (position + 1)
     int32_t* counts;    // selected rows per sequence [B]
     uint32_t* status;   // validation status word

@@ -78,6 +78,7 @@ struct PrepArgs {
     void* kv_dst; long long kd_sb, kd_st;
     void* pe_dst; long long pd_sb, pd_st;
     void* qt;
+    void* qlo;          // bf16 path: low parts of the rotated query [B][H][64]
     int32_t* list;
     int32_t* counts;
     uint32_t* status;
@@ -168,20 +169,29 @@ template <typename QtT>
 __device__ __forceinline__ void rotate32(const PrepArgs& a, int b, int h, int f0, const float (&x)[32],
                                          const float (&t)[32]) {
     QtT* dst = (QtT*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f0;
+    float yf[32];
     QtT y[32];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const float c = t[2 * i], sn = t[2 * i + 1];
-        y[2 * i] = from_f32<QtT>(x[2 * i] * c - x[2 * i + 1] * sn);
-        y[2 * i + 1] = from_f32<QtT>(x[2 * i] * sn + x[2 * i + 1] * c);
+        yf[2 * i] = x[2 * i] * c - x[2 * i + 1] * sn;
+        yf[2 * i + 1] = x[2 * i] * sn + x[2 * i + 1] * c;
+        y[2 * i] = from_f32<QtT>(yf[2 * i]);
+        y[2 * i + 1] = from_f32<QtT>(yf[2 * i + 1]);
     }
     if constexpr (sizeof(QtT) == 2) {
+        // high part into Q~, the remainder (rounded to bf16) beside it
+        bf16* lo = (bf16*)a.qlo + ((long long)b * a.H + h) * D_ROPE + f0;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            bf16x8 v;
+            bf16x8 v, r;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = y[8 * k + j];
+            for (int j = 0; j < 8; ++j) {
+                v[j] = y[8 * k + j];
+                r[j] = f2bf(yf[8 * k + j] - (float)y[8 * k + j]);
+            }
             *(bf16x8*)(dst + 8 * k) = v;
+            *(bf16x8*)(lo + 8 * k) = r;
         }
     } else {
 #pragma unroll
@@ -539,7 +549,7 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     a.pe_new = p.pe_new; a.pn_sb = p.pe_new_stride_b;
     a.kv_dst = const_cast<void*>(p.kv_cache); a.kd_sb = p.kv_stride_b; a.kd_st = p.kv_stride_t;
     a.pe_dst = const_cast<void*>(p.pe_cache); a.pd_sb = p.pe_stride_b; a.pd_st = p.pe_stride_t;
-    a.qt = w.qt; a.list = w.list; a.counts = w.counts; a.status = w.status;
+    a.qt = w.qt; a.qlo = w.qlo; a.list = w.list; a.counts = w.counts; a.status = w.status;
     const dim3 grid(a.n_absorb + p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;
     if (plan.bf16_path) {

@@ -33,6 +33,7 @@ hipError_t launch_rope_freqs(const mla_rope_cfg_t&, float*, hipStream_t) { ++g_l
 hipError_t launch_prep(const mla_decode_params_t& p, const Plan& pl, const Work& w, bool, hipStream_t) {
     ++g_launches;
     memset(w.qt, 0, (size_t)p.B * p.H * 576 * act_bytes(pl));
+    if (pl.bf16_path) memset(w.qlo, 0, (size_t)p.B * p.H * 64 * 2);
     memset(w.list, 0, (size_t)p.B * p.K * 4);
     memset(w.counts, 0, (size_t)p.B * 4);
     memset(w.status, 0, 4);

@@ -1,16 +1,17 @@
 """Decode inputs whose scores spread far beyond the N(0, 1) workloads.
 
 With N(0, 1) queries and caches the scaled scores of one head stay within a
-few units of each other.  A legal input can spread them much further: here,
-for one target head h0 per sequence, a chosen set of selected rows gets the
-latent C[t] = -alpha * u, u the unit vector along that head's absorbed query
-q_abs = q_nope[b, h0] . W_UK[h0], so its score sits about c_log2 units
-(log2 domain) below the rows left untouched.  Every other head sees those
-rows at an ordinary, random score.
+few units of each other.  A legal input can spread them much further.  Here
+a chosen set of selected rows of each sequence gets the latent
+C[t] = alpha * u, where u is the least-norm vector with q_abs_h . u = -1 for
+every head h (q_abs_h = q_nope[b, h] . W_UK[h]), so that the latent part of
+those rows' scores is -alpha * scale for all heads at once: about c_log2
+units (log2 domain) below the rows left untouched, whose scores stay
+ordinary.
 
   mode "late":  every selected row except the 3 highest positions is pushed
-                down: the maximum of h0 comes from the last rows of the
-                last split, far above its first 32 rows.
+                down: the maximum of every head comes from the last rows of
+                the last split, far above that split's first 32 rows.
   mode "first": every selected row except the 32 lowest positions is pushed
                 down: the first rows hold the maximum and every later row
                 lies far below it.
@@ -77,14 +78,14 @@ def build(name, mode, c_log2, dtype_act="bf16", dtype_w="bf16", seed=41, H=128, 
     cfg = oracle.RopeConfig(**w.rope)
     scale = oracle.softmax_scale(192, cfg)
     for b in range(w.B):
-        h0 = (37 + 63 * b) % H
         row = w.topk_indices[b]
         sel = np.unique(row[row >= 0])
-        qa = w.q_nope[b, h0].astype(np.float64) @ w.w_uk[h0].astype(np.float64)
-        norm = np.linalg.norm(qa)
-        alpha = c_log2 * LN2 / (norm * scale)
+        qa = np.einsum("hd,hdc->hc", w.q_nope[b].astype(np.float64), w.w_uk.astype(np.float64))
+        # least-norm u with qa @ u = -1 for every head
+        u = -qa.T @ np.linalg.solve(qa @ qa.T, np.ones(w.H))
+        alpha = c_log2 * LN2 / scale
         target = sel[:-3] if mode == "late" else sel[32:]
-        w.kv_cache[b, target] = (-alpha * qa / norm).astype(np.float32)
+        w.kv_cache[b, target] = (alpha * u).astype(np.float32)
     if dtype_act == "bf16":
         W.round_bf16(w.kv_cache)
     return w

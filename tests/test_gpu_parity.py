@@ -178,18 +178,19 @@ def test_bf16_output():
 # scores, excerpt mla-decode).  The bf16 kernel exponentiates against the
 # floored maximum of each split's first 32 rows and redoes a split with the
 # exact maximum when a later score lies more than 64 units (log2) above it.
-#   late150: 150 units above: 2^150 overflows fp32, so a correct result
-#            shows the second pass ran;
-#   late90:  above the limit but below overflow;
-#   late60:  just under the limit: the first pass stands, with
+# The inputs push chosen rows down by c units for every head at once:
+#   late150: the 3 last rows lie ~156 units above the rest: 2^156 overflows
+#            fp32, so a correct result shows the second pass ran;
+#   late90:  ~96 units: above the limit but below overflow;
+#   late54:  ~60 units, just under the limit: the first pass stands, with
 #            probabilities up to 2^60;
-#   first200: the first rows hold the maximum and every later row of the
-#            target head lies 200 units below (its probability underflows).
+#   first200: the first 32 rows hold the maximum and every later row lies
+#            ~200 units below it (its probability underflows to zero).
 # Each with one split and with three (the last split holds the maximum).
 # ---------------------------------------------------------------------------
 import spread_inputs as SI  # noqa: E402
 
-SPREAD = [("late", 150), ("late", 90), ("late", 60), ("first", 200)]
+SPREAD = [("late", 150), ("late", 90), ("late", 54), ("first", 200)]
 
 
 @pytest.mark.parametrize("mode,c", SPREAD, ids=[f"{m}{c}" for m, c in SPREAD])
@@ -369,13 +370,18 @@ def test_split_count_invariance():
         _check(dev, out, lse)
     base, base_lse = outs[1]
     for S, (out, lse) in outs.items():
-        # Splitting changes where partial sums are rounded to bf16 (each split's
-        # normalised partial once, then the merged latent), so outputs move by
-        # bf16 rounding noise only: bounded by the same 1e-2 as the parity bar.
-        # The log-sum-exp is formed from fp32 sums and agrees to fp32 rounding.
+        # Every plan rounds the same probabilities to bf16 (the reference
+        # maximum is floored, so moving a split boundary scales them by powers
+        # of two only).  What differs is where latent sums are rounded to bf16:
+        # each split's normalised partial, then the merged latent, i.e. two
+        # roundings of at most 2^-9 relative per element in each plan.  Their
+        # difference stays within 4e-3 per output row (about 3.6e-3 at most
+        # on these inputs), well inside the 1e-2 parity bar; a dropped,
+        # doubled or misweighted split moves rows by far more.  The log-sum-
+        # exp is formed from fp32 sums and agrees to fp32 rounding.
         err = rel_l2_rows(out.cpu().numpy(), base.cpu().numpy()).max()
         print(f"splits {S}: max rel L2 vs one split {err:.3e}", flush=True)
-        assert err <= 1e-2, (S, err)
+        assert err <= 4e-3, (S, err)
         assert (lse - base_lse).abs().max().item() <= 1e-5
 
 

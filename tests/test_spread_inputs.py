@@ -8,7 +8,7 @@ CASES = [
     # mode, c_log2, bound on the largest excess of the last split over its first-tile floor
     ("late", 150, lambda e: e > 140),        # beyond fp32's exponent range: needs the exact maximum
     ("late", 90, lambda e: 70 < e < 120),    # above the first-pass limit of 64, below overflow
-    ("late", 60, lambda e: 55 < e < 62.5),   # just under the limit: stays on the first pass
+    ("late", 54, lambda e: 55 < e < 62.5),   # just under the limit: stays on the first pass
 ]
 
 
@@ -20,23 +20,36 @@ def test_late_maximum_cases(mode, c, ok, splits):
         ex = SI.excess_log2(w, b, splits)
         assert ok(ex[-1]), (b, ex)
         # the earlier splits hold only pushed-down rows: ordinary spreads
-        assert all(e < 30 for e in ex[:-1]), (b, ex)
+        assert all(e < 20 for e in ex[:-1]), (b, ex)
 
 
 @pytest.mark.parametrize("splits", [1, 3])
 def test_first_tile_maximum_case(splits):
+    import numpy as np
     w = SI.build("spread_first200", "first", 200)
     for b in range(w.B):
-        h0 = (37 + 63 * b) % w.H
         row = w.topk_indices[b]
-        import numpy as np
         sel = np.unique(row[row >= 0])
-        x = SI.scores_log2(w, b, sel)[h0]
-        # every row after the first 32 lies at least 150 units below the first rows' maximum,
-        # so its probability underflows (2^-150 is below fp32's smallest subnormal)
-        assert x[32:].max() < x[:32].max() - 150
+        x = SI.scores_log2(w, b, sel)
+        # for every head, every row after the first 32 lies at least 180 units
+        # below the first rows' maximum: its probability underflows (2^-149 is
+        # fp32's smallest subnormal)
+        assert (x[:, 32:].max(axis=1) < x[:, :32].max(axis=1) - 180).all()
         # no split's first pass exceeds the limit
-        assert max(SI.excess_log2(w, b, splits)) < 60
+        assert max(SI.excess_log2(w, b, splits)) < 20
+
+
+def test_pushed_rows_are_low_for_every_head():
+    import numpy as np
+    w = SI.build("spread_late150", "late", 150)
+    for b in range(w.B):
+        row = w.topk_indices[b]
+        sel = np.unique(row[row >= 0])
+        x = SI.scores_log2(w, b, sel)
+        # pushed rows: about -150 for every head (rotary noise of a few units
+        # on top); the three late rows stay ordinary
+        assert (x[:, :-3] < -130).all() and (x[:, :-3] > -170).all()
+        assert (np.abs(x[:, -3:]) < 20).all()
 
 
 def test_split_ranges_cover_the_list():
