@@ -77,6 +77,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 namespace mla {
 
+int set_error(int code, const char* msg) {
+    snprintf(g_err, sizeof g_err, "%s", msg);
+    return code;
+}
+
 size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* base, Work* w) {
     const size_t act = bf16_path ? 2 : 4;
     size_t off = 0;

@@ -30,6 +30,9 @@ struct Work {
     size_t bytes;       // total bytes used
 };
 
+// Sets the calling thread's last error message; returns code.
+int set_error(int code, const char* msg);
+
 // Sizes of the workspace regions; returns the total (0 on overflow).
 size_t workspace_layout(int B, int H, int K, bool bf16_path, int splits, void* base, Work* w);
 

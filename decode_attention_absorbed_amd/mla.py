@@ -95,6 +95,8 @@ def lib():
         L.mla_decode_workspace_size.restype = ctypes.c_size_t
         L.mla_decode_attn.argtypes = [ctypes.POINTER(DecodeParams), _P]
         L.mla_decode_attn.restype = ctypes.c_int
+        L.mla_decode_attn_noalloc.argtypes = [ctypes.POINTER(DecodeParams), _P]
+        L.mla_decode_attn_noalloc.restype = ctypes.c_int
         L.mla_decode_params_size.argtypes = []
         L.mla_decode_params_size.restype = ctypes.c_size_t
         L.mla_topk.argtypes = [ctypes.POINTER(TopkParams), _P]
@@ -304,6 +306,18 @@ def build_params(q_nope, q_pe, w_uk, w_uv, kv_cache, pe_cache, topk_indices, cac
 def decode_attn(params: DecodeParams, stream=None, check=True) -> int:
     """Run mla_decode_attn; raises MLAError on a non-zero code when check."""
     rc = lib().mla_decode_attn(ctypes.byref(params), _stream_handle(stream))
+    if check and rc != MLA_OK:
+        raise MLAError(rc, last_error(), params.validate_status)
+    return rc
+
+
+MLA_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_attn_noalloc(params: DecodeParams, stream=None, check=True) -> int:
+    """Run mla_decode_attn_noalloc (scratch in the library's own per-device
+    buffer; params.workspace is ignored); raises MLAError when check."""
+    rc = lib().mla_decode_attn_noalloc(ctypes.byref(params), _stream_handle(stream))
     if check and rc != MLA_OK:
         raise MLAError(rc, last_error(), params.validate_status)
     return rc

@@ -239,6 +239,29 @@ int mla_decode_attn(mla_decode_params_t* p, void* stream);
  * can check its own struct layout before the first call. */
 size_t mla_decode_params_size(void);
 
+/* Bytes of the scratch buffer mla_decode_attn_noalloc uses on each device. */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * mla_decode_attn_noalloc -- mla_decode_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, kernels, arguments and
+ * return codes as mla_decode_attn, except that p->workspace and
+ * p->workspace_size are ignored: the scratch memory is a buffer of
+ * MLA_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs
+ * on (in its code object, until the process ends).  The caller still owns
+ * and passes every input and output.
+ *   - Sizes whose mla_decode_workspace_size exceeds MLA_NOALLOC_SCRATCH_BYTES
+ *     return MLA_ERR_WORKSPACE with nothing launched (the ragged batch of
+ *     128 sequences x 128 heads x 2048 selected rows needs about 56 MB).
+ *   - The first call on a device looks up that device's buffer address with
+ *     hipGetSymbolAddress (with the device current); no call allocates.
+ *   - Every call on one device shares its buffer and nothing in it needs
+ *     clearing between calls.  Calls that overlap in time on one device
+ *     (different streams or threads) race on the buffer: serialise them.
+ */
+int mla_decode_attn_noalloc(mla_decode_params_t* p, void* stream);
+
 /* ---- top-k selection ---------------------------------------------------- */
 typedef struct mla_topk_params {
     int32_t B;                 /* sequences, 1..2^20 */

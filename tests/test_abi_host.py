@@ -284,3 +284,14 @@ def test_binding_rejects_bad_topk_and_rope_tensors():
         m.rope_apply(x, torch.zeros(8, dtype=torch.int32), table.double(), True)
     with pytest.raises(m.MLAError):
         m.rope_apply(x, torch.zeros(8, dtype=torch.int32), table, True)        # host tensors
+
+
+def test_noalloc_size_limit_host(mla):
+    # the allocation-free entry point refuses sizes beyond its buffer before
+    # it touches the device (no GPU needed for this path)
+    p = _params(mla, B=4096, K=2048, num_splits=8, idx_stride_b=2048)
+    assert mla.lib().mla_decode_attn_noalloc(ctypes.byref(p), None) == mla.MLA_ERR_WORKSPACE
+    assert "scratch" in mla.last_error()
+    assert mla.lib().mla_decode_attn_noalloc(None, None) == mla.MLA_ERR_INVALID_ARG
+    need = mla.workspace_size(128, 128, 2048, mla.MLA_DTYPE_BF16, mla.MLA_DTYPE_F32, 256, 0)
+    assert 0 < need <= mla.MLA_NOALLOC_SCRATCH_BYTES     # the ragged batch fits
