@@ -91,8 +91,15 @@ static_assert(STAGE % 256 == 0 && OFF_Q % 16 == 0, "alignment");
 // Copies per wave per tile: one index fetch, 8 latent rows, one rotary copy.
 constexpr int COPIES_PER_TILE = 10;
 
-// The wave index, known to the compiler as wave-uniform (an SGPR).
-__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+// threadIdx.x through an empty asm statement, read once per pass: values
+// derived from it (lane offsets, addresses) are then computed inside the
+// pass instead of being hoisted out of the pass loop, where they would stay
+// live across the whole tile loop and spill.
+__device__ __forceinline__ int tid_opaque() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
 // Largest exponent (log2) a probability may reach relative to the
 // reference maximum before the split is recomputed with the exact maximum.
@@ -133,8 +140,7 @@ struct LaneOffsets {
     uint32_t lat, rcp;
 };
 
-__device__ __forceinline__ LaneOffsets lane_offsets(const AttnArgs& a) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ LaneOffsets lane_offsets(const AttnArgs& a, int lane, int wave) {
     const int g = lane >> 5, l32 = lane & 31;
     LaneOffsets lo;
     lo.qk = row_start(l32) + 16 * g;
@@ -162,8 +168,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const AttnArgs& a) {
 // Row indices of tile T for this wave: lanes 0..7 copy 4 bytes each into the
 // ring slot.  The list descriptor's window is the split's rows, so positions
 // past its end read 0 ("no row").
-__device__ __forceinline__ void fetch_idx(const SplitCtx& sc, int T, int* __restrict__ slot) {
-    const int lane = threadIdx.x & 63, wave = wave_id();
+__device__ __forceinline__ void fetch_idx(const SplitCtx& sc, int T, int* __restrict__ slot, int lane, int wave) {
     if (lane < 8) buffer_to_lds4(sc.list, (uint32_t)(T * R + wave * 8 + lane) * 4u, (MLA_LDS void*)slot);
 }
 
@@ -173,8 +178,7 @@ struct TileRows {
     uint32_t rot;       // row 8 wave + lane/8 (rotary copy)
 };
 
-__device__ __forceinline__ TileRows read_rows(const int* __restrict__ slot) {
-    const int lane = threadIdx.x & 63;
+__device__ __forceinline__ TileRows read_rows(const int* __restrict__ slot, int lane) {
     TileRows tr;
     tr.i0 = *(const u32x4*)slot;
     tr.i1 = *(const u32x4*)(slot + 4);
@@ -193,18 +197,18 @@ __device__ __forceinline__ void issue_row(const AttnArgs& a, const SplitCtx& sc,
 
 // Copy the rotary parts (128 bytes each) of this wave's 8 rows.
 __device__ __forceinline__ void issue_rot(const AttnArgs& a, const SplitCtx& sc, const LaneOffsets& lo,
-                                          MLA_LDS char* __restrict__ stage, const TileRows& tr) {
-    const int wave = wave_id();
+                                          MLA_LDS char* __restrict__ stage, const TileRows& tr, int wave) {
     buffer_to_lds16(sc.pe, lo.rcp + tr.rot * ((uint32_t)a.pe_st * 2u), (MLA_LDS void*)(stage + LATB + wave * 1024));
 }
 
 // All 9 copies of this wave's part of a tile (prologue).
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const SplitCtx& sc, const LaneOffsets& lo,
-                                           const int (&mst)[8], MLA_LDS char* stage, const int* __restrict__ slot) {
-    const TileRows tr = read_rows(slot);
+                                           const int (&mst)[8], MLA_LDS char* stage, const int* __restrict__ slot,
+                                           int lane, int wave) {
+    const TileRows tr = read_rows(slot, lane);
 #pragma unroll
     for (int j = 0; j < 8; ++j) issue_row(a, sc, lo, stage + mst[j], tr, j);
-    issue_rot(a, sc, lo, stage, tr);
+    issue_rot(a, sc, lo, stage, tr, wave);
 }
 
 // v_mfma_f32_32x32x16_bf16 with the accumulator pinned to VGPRs.  The 256
@@ -330,14 +334,13 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
                                           const char* __restrict__ smem_q, const LaneOffsets& lo,
                                           const bf16x8 (&qreg)[QK_REG], const bf16x8 (&qlo)[NLO], PassState& ps,
                                           bf16x8 (&ring)[RING], bf16x8& ptail, float scale_log2, int rem, bool first,
-                                          Hook&& hook) {
+                                          int g, Hook&& hook) {
     int qb = lo.qk, rb = lo.rot, t0 = lo.tr[0], t1 = lo.tr[1], qo = lo.q;
     opaque(qb);
     opaque(rb);
     opaque(t0);
     opaque(t1);
     opaque(qo);
-    const int g = (threadIdx.x & 63) >> 5;
     auto pv_load = [&](int p) -> bf16x8 {
         if (p >= 32) return pv_operand(cur, t0, t1, 1, p - 32);        // next tile's tail
         if (p < 16) return pv_operand(prv, t0, t1, 1, p);               // tail: previous tile, K step 1
@@ -436,7 +439,7 @@ __device__ __forceinline__ void pv_last(const char* __restrict__ prv, const Lane
 // tile it+3 and tile it+1) may still be in flight.
 __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc, char* smem,
                                           float& m_ref, bool known) {
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int tid = tid_opaque(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int nt = sc.ntiles;
     int* flag = (int*)(smem + OFF_FLAG);
@@ -449,7 +452,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     auto lstage = [&](int T) { return lsm + stage(T); };
     auto slot = [&](int T) { return idx_ring + (T % NSLOT) * 32; };
 
-    const LaneOffsets lo = lane_offsets(a);
+    const LaneOffsets lo = lane_offsets(a, lane, wave);
     int mst[8];                                    // row_start of this wave's 8 rows
 #pragma unroll
     for (int j = 0; j < 8; ++j) mst[j] = __builtin_amdgcn_readfirstlane(row_start(wave * 8 + j));
@@ -477,7 +480,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     bf16x8 qlo[NLO];
     if (nt > 0) {
 #pragma unroll
-        for (int T = 0; T < 2; ++T) fetch_idx(sc, T, slot(T));
+        for (int T = 0; T < 2; ++T) fetch_idx(sc, T, slot(T), lane, wave);
         {
             // LDS part: lane l fills bytes 16 l of the wave's 1 KB row of
             // block i, i.e. head 32 wave + l/2, features 16 (QK_REG + i) + 8 (l & 1)
@@ -501,8 +504,8 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
         wait_vmcnt<QK_LDS + QK_REG + NLO>();       // the two index fetches (issued first) landed
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-            fetch_idx(sc, T + 2, slot(T + 2));
-            issue_tile(a, sc, lo, mst, lstage(T), slot(T));
+            fetch_idx(sc, T + 2, slot(T + 2), lane, wave);
+            issue_tile(a, sc, lo, mst, lstage(T), slot(T), lane, wave);
         }
     }
 
@@ -521,15 +524,15 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     for (int it = 0; it < nt; ++it) {
         wait_vmcnt<COPIES_PER_TILE>();
         lds_barrier();          // tile it resident and visible; stage (it-2)%4 free
-        const TileRows rows = read_rows(slot(it + 2));
+        const TileRows rows = read_rows(slot(it + 2), lane);
         MLA_LDS char* const dst = lstage(it + 2);
         int* const fslot = slot(it + 4);
         tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, qlo, ps, ring, ptail, a.scale_log2,
-                  nrows - it * R, it == 0 && !known, [&](int st_) {
+                  nrows - it * R, it == 0 && !known, g, [&](int st_) {
             // copies of tile it+2 spread over the tile's 68 MFMA steps
-            if (st_ == 1) fetch_idx(sc, it + 4, fslot);
+            if (st_ == 1) fetch_idx(sc, it + 4, fslot, lane, wave);
             if (st_ >= 3 && st_ <= 59 && (st_ - 3) % 8 == 0) issue_row(a, sc, lo, dst + mst[(st_ - 3) / 8], rows, (st_ - 3) / 8);
-            if (st_ == 63) issue_rot(a, sc, lo, dst, rows);
+            if (st_ == 63) issue_rot(a, sc, lo, dst, rows, wave);
         });
     }
     if (nt > 0) pv_last(smem + stage(nt - 1), lo, ps, ring, ptail);
