@@ -294,7 +294,7 @@ __device__ __forceinline__ void soft2(const f32x16& acc, int i, float m_ref, flo
 // tile (its first reads are issued during steps 3..7).
 constexpr int RING = 4;
 constexpr int PV_AHEAD = RING - 1;
-constexpr int QK_AHEAD = 3;
+constexpr int QK_AHEAD = 5;
 // The QK^T chain: the 32 latent feature blocks, then each of the 4 rotary
 // blocks twice, against the high and then the low bf16 part of the rotary
 // query (q^ = hi + lo to 16 significant bits: its rounding to bf16 would
@@ -308,11 +308,13 @@ static_assert(32 % RING == 0, "ring alignment");
 __host__ __device__ constexpr int chain_block(int j) { return j < 32 ? j : 32 + (j - 32) / 2; }
 __host__ __device__ constexpr bool chain_lo(int j) { return j >= 32 && ((j - 32) & 1) != 0; }
 // K operands of the chain live in a ring of QK_AHEAD + 1 slots indexed by
-// block: block j + QK_AHEAD is loaded while block j is in use, and the
-// rotary blocks, used twice, are loaded QK_AHEAD chain steps before their
-// first use, when the block four before them is already dead.
+// block.  Block b + KRING, loaded QK_AHEAD chain steps before its first use,
+// replaces block b only after b's last use: for latent blocks that is
+// KRING > QK_AHEAD; a rotary block (first used at 32 + 2 (b - 32), twice)
+// lands KRING - QK_AHEAD >= 1 steps after the last use of the block KRING
+// before it, and no rotary block has a successor KRING blocks later.
 constexpr int KRING = QK_AHEAD + 1;
-static_assert(KRING == 4, "the rotary blocks' reuse is checked for a ring of 4");
+static_assert(KRING > QK_AHEAD && KRING >= NLO, "operand ring");
 
 // A operand of PV step (kt, cb) of the tile in stage st.
 __device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0, int t1, int kt, int cb) {
