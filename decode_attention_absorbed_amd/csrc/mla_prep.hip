@@ -349,26 +349,48 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // q_abs for head h, latent columns [256*half, 256*half + 256), every
 // sequence, with bf16 MFMA: M = latent columns, N = sequences (32 per
 // step), K = the 128 content features.  Wave w owns 64 columns.  Its
-// weight slice W_UK[h][0:128][64 columns] is read once with 16-byte loads,
-// converted to bf16 (fp32 weights split into a bf16 high part and a bf16
-// remainder, two MFMAs each, so they enter with ~16 significant bits) and
-// passed through a wave-private LDS region, 64 feature rows at a time, to
-// be read back transposed (8 consecutive features of one column per lane,
-// ds_read_b64_tr_b16).  The queries q_nope[:, h, :] of up to 128 sequences
-// are copied into LDS once per block (buffer->LDS, issued together with the
-// weight loads) and shared by the 4 waves.
-constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // one staging round: [64 rows][64 columns] bf16
+// weight slice W_UK[h][0:128][64 columns] is read once per 128 sequences
+// with 16-byte loads, in eight chunks of 16 feature rows, two chunks in
+// flight.  Each chunk, as it lands, is converted to bf16 (fp32 weights
+// split into a bf16 high part and a bf16 remainder, two MFMAs each, so they
+// enter with ~16 significant bits), passed through a wave-private LDS region
+// to be read back transposed (8 consecutive features of one column per
+// lane, ds_read_b64_tr_b16), and multiplied at once into the accumulators
+// of all (up to 128) sequences, so the MFMA work runs under the later
+// chunks' loads.  The queries q_nope[:, h, :] of up to 128 sequences are
+// copied into LDS once per block (buffer->LDS, issued before the weight
+// loads) and shared by the 4 waves.
+constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // a wave's staging region (32 of its 64 rows used)
 constexpr int ABS_QROWS = 128;                        // sequences per query chunk
 constexpr int ABS_Q_OFF = 4 * ABS_WAVE_LDS;           // query chunk: [128][128] bf16, 256 B rows
+constexpr int ABS_CHUNKS = D_NOPE / 16;               // weight chunks of 16 feature rows (one K step)
+constexpr int ABS_AHEAD = 2;                          // chunks in flight
 
+// s_barrier after this wave's LDS operations, without waiting for its
+// loads in flight (__syncthreads() waits for those too).
+__device__ __forceinline__ void lds_barrier_only() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// The thread index through an empty asm statement: lane-derived addresses
+// are then computed inside the sequence-group loop instead of being hoisted
+// out of it, where they would each hold a register for the whole loop.
+__device__ __forceinline__ int tid_opaque() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
+// Sequences [b0, b0 + 128) of head h, latent half `half`.
 template <typename WT>
-__device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
+__device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half, char* lds, int b0) {
     constexpr int NP = sizeof(WT) == 4 ? 2 : 1;       // weight parts
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = tid_opaque(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
     const WT* W = (const WT*)a.w_uk + h * a.wk_sh + c0;
-    char* wl = lds + wave * ABS_WAVE_LDS;             // row d (0..63), column c at d*128 + c*2 (swizzled)
+    char* wl = lds + wave * ABS_WAVE_LDS;             // row d, column c at d*128 + c*2 (swizzled)
     const char* ql = lds + ABS_Q_OFF;
     // Staging row d holds 64 columns = 8 chunks of 16 bytes; chunk q sits at
     // slot q ^ (d & 7) so that the transposed reads (4 rows x 16 columns per
@@ -392,105 +414,141 @@ __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
             buffer_to_lds16(qs, off, (MLA_LDS void*)(lds + ABS_Q_OFF + (8 * wave + i) * 1024));
         }
     };
-    // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i,
-    // all 32 loads in flight at once, issued before the first query chunk's
-    // copies.
+    // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i;
+    // loads [4c, 4c + 4) hold feature rows [16c, 16c + 16) (chunk c).
     const int cq = 4 * (lane & 15);
     float wv[D_NOPE / 4][4];
+    auto load_chunk = [&](int c) {
 #pragma unroll
-    for (int i = 0; i < D_NOPE / 4; ++i) {
-        const int d = (lane >> 4) + 4 * i;
-        if constexpr (sizeof(WT) == 4) {
-            const f32x4 x = *(const f32x4*)(W + d * RANK + cq);
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * c + ii, d = (lane >> 4) + 4 * i;
+            if constexpr (sizeof(WT) == 4) {
+                const f32x4 x = *(const f32x4*)(W + d * RANK + cq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[i][e] = x[e];
-        } else {
-            const bf16x4 x = *(const bf16x4*)(W + d * RANK + cq);
+                for (int e = 0; e < 4; ++e) wv[i][e] = x[e];
+            } else {
+                const bf16x4 x = *(const bf16x4*)(W + d * RANK + cq);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[i][e] = (float)x[e];
+                for (int e = 0; e < 4; ++e) wv[i][e] = (float)x[e];
+            }
         }
-    }
-    copy_q(0);
-    // bf16 parts, packed right away so the fp32 values die early
-    bf16x4 wp[NP][D_NOPE / 4];
-#pragma unroll
-    for (int i = 0; i < D_NOPE / 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bf16 hi = (bf16)wv[i][e];
-            wp[0][i][e] = hi;
-            if constexpr (NP == 2) wp[NP - 1][i][e] = (bf16)(wv[i][e] - (float)hi);
-        }
-    // Weight operand (A) of K step kb, column block nb: lane l holds column
-    // 32 nb + l%32, features 16 kb + 8 (l/32) .. +7 -- two transposed reads of
-    // 4 rows each.  In a 16-lane block, lane 4j + q addresses row
-    // 16 kb + 8 (blk >> 1) + 4 rr + j, columns 32 nb + 16 (blk & 1) + 4 q .. +3.
+    };
+    // Weight operand (A) of the chunk's K step, column block nb: lane l holds
+    // column 32 nb + l%32, features 8 (l/32) .. +7 of the chunk -- two
+    // transposed reads of 4 rows each.  In a 16-lane block, lane 4j + q
+    // addresses local row 8 (blk >> 1) + 4 rr + j, columns
+    // 32 nb + 16 (blk & 1) + 4 q .. +3.
     const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
-    bf16x8 bw[NP][2][8];
-    // The staging rounds (part pp, feature rows 64 hf .. 64 hf + 63) pass
-    // through the wave's LDS region one after the other.  A wave's LDS
-    // accesses run in order, so a round's writes follow the previous round's
-    // reads.
+
+    const int nrow = min(ABS_QROWS, a.B - b0);
+    {
+        // The query copies go out before the weight loads, so the wait for
+        // the first weight chunk covers them too.
+        copy_q(b0);
+        asm volatile("" ::: "memory");
 #pragma unroll
-    for (int pp = 0; pp < NP; ++pp)
+        for (int c = 0; c < ABS_AHEAD; ++c) load_chunk(c);
+        f32x16 acc[ABS_QROWS / 32][2];
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+        for (int bt = 0; bt < ABS_QROWS / 32; ++bt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) *(bf16x4*)(wl + waddr((lane >> 4) + 4 * i, cq)) = wp[pp][16 * hf + i];
+            for (int nb = 0; nb < 2; ++nb) acc[bt][nb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < ABS_CHUNKS; ++c) {
+            if (c == 0) wait_vmcnt<4 * (ABS_AHEAD - 1)>();   // query copies and chunk 0 landed
+            bf16x4 wp[NP][4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 4 * c + ii;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bf16 hi = (bf16)wv[i][e];
+                    wp[0][ii][e] = hi;
+                    if constexpr (NP == 2) wp[NP - 1][ii][e] = (bf16)(wv[i][e] - (float)hi);
+                }
+            }
+            if (c + ABS_AHEAD < ABS_CHUNKS) {
+                asm volatile("" ::: "memory");        // issue chunk c + AHEAD here, not earlier
+                load_chunk(c + ABS_AHEAD);
+            }
+            // Part pp of the chunk at local rows 16 pp .. 16 pp + 15.  A wave's
+            // LDS accesses run in order, so these writes follow the previous
+            // chunk's reads.
+#pragma unroll
+            for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) *(bf16x4*)(wl + waddr(16 * pp + (lane >> 4) + 4 * ii, cq)) = wp[pp][ii];
             __builtin_amdgcn_s_waitcnt(0xC07F);       // this wave's writes done (only it reads them)
             asm volatile("" ::: "memory");
+            bf16x8 bw[NP][2];
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
+            for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4) {
+                for (int nb = 0; nb < 2; ++nb) {
                     bf16x4 r[2];
 #pragma unroll
                     for (int rr = 0; rr < 2; ++rr) {
-                        const int d = 16 * k4 + 8 * (blk >> 1) + 4 * rr + jj;
-                        const int c = 32 * nb + 16 * (blk & 1) + 4 * qq;
-                        r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(d, c)));
+                        const int d = 16 * pp + 8 * (blk >> 1) + 4 * rr + jj;
+                        const int cc = 32 * nb + 16 * (blk & 1) + 4 * qq;
+                        r[rr] = lds_read_tr16((const MLA_LDS void*)(wl + waddr(d, cc)));
                     }
-                    bw[pp][nb][4 * hf + k4] = cat(r[0], r[1]);
+                    bw[pp][nb] = cat(r[0], r[1]);
                 }
-            __builtin_amdgcn_s_waitcnt(0xC07F);       // reads done before the next round overwrites
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // reads done before the next chunk overwrites
             asm volatile("" ::: "memory");
+            if (c == 0) lds_barrier_only();           // every wave's query copies visible
+#pragma unroll
+            for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+                if (32 * bt < nrow) {
+                    const int r = 32 * bt + l32;
+                    const bf16x8 aq = *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4));
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+                        for (int pp = 0; pp < NP; ++pp) acc[bt][nb] = mfma32(bw[pp][nb], aq, acc[bt][nb]);
+                }
+            }
         }
-
-    for (int b0 = 0; b0 < a.B; b0 += ABS_QROWS) {
-        if (b0 > 0) {
-            __syncthreads();                          // every wave done with the previous chunk
-            copy_q(b0);
-        }
-        wait_vmcnt<0>();
-        __syncthreads();                              // the chunk's rows visible to every wave
-        const int nb0 = min(ABS_QROWS, a.B - b0);
-        for (int s0 = 0; s0 < nb0; s0 += 32) {
-            const int r = s0 + l32, bA = b0 + r;
-            bf16x8 aq[8];
+        // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
+        // sequence 32 bt + l%32 and columns 8(i/4) + 4(l/32) + i%4 of block nb.
+        // Each batch passes through the wave's LDS region as [32 sequences]
+        // [64 columns] (16-byte chunk k of row r at slot k ^ (r & 7)) and is
+        // read back so that 8 lanes write one sequence's 128 contiguous bytes.
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) aq[kb] = *(const bf16x8*)(ql + r * 256 + (((2 * kb + g) ^ (r & 15)) << 4));
-            // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l
-            // holds sequence bA and columns 8(i/4) + 4(l/32) + i%4, so each lane
-            // writes 4 consecutive bf16 (8 bytes) per group of 4 accumulators.
+        for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (32 * bt < nrow) {
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                f32x16 acc = {};
-#pragma unroll
-                for (int kb = 0; kb < 8; ++kb)
-#pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) acc = mfma32(bw[pp][nb][kb], aq[kb], acc);
-                if (bA < a.B) {
-                    bf16* dst = (bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 32 * nb + 4 * g;
+                for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                     for (int i4 = 0; i4 < 4; ++i4) {
                         bf16x4 v;
 #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) v[rr] = f2bf(acc[4 * i4 + rr]);
-                        *(bf16x4*)(dst + 8 * i4) = v;
+                        for (int rr = 0; rr < 4; ++rr) v[rr] = f2bf(acc[bt][nb][4 * i4 + rr]);
+                        const int k = 4 * nb + i4;             // 16-byte chunk of the 64 columns
+                        *(bf16x4*)(wl + l32 * 128 + ((k ^ (l32 & 7)) << 4) + 8 * g) = v;
                     }
+                __builtin_amdgcn_s_waitcnt(0xC07F);
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = (lane >> 3) + 8 * j, k = lane & 7;
+                    const bf16x8 v = *(const bf16x8*)(wl + r * 128 + ((k ^ (r & 7)) << 4));
+                    const int bA = b0 + 32 * bt + r;
+                    if (bA < a.B) *(bf16x8*)((bf16*)a.qt + ((long long)bA * a.H + h) * ROW + c0 + 8 * k) = v;
                 }
+                __builtin_amdgcn_s_waitcnt(0xC07F);           // reads done before the next batch overwrites
+                asm volatile("" ::: "memory");
             }
         }
+    }
+}
+
+template <typename WT>
+__device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
+    for (int b0 = 0; b0 < a.B; b0 += ABS_QROWS) {
+        if (b0 > 0) __syncthreads();                  // every wave done with the previous query chunk
+        absorb_group<WT>(a, h, half, lds, b0);
     }
 }
 
@@ -522,8 +580,11 @@ static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 
 // Blocks [0, B) prepare one sequence each (selection, rotary query); blocks
 // [B, B + 2H) compute absorption slice bid - B (head (bid-B)/2, half (bid-B)%2).
+// Two blocks per CU (64 KB of LDS each) need at most 256 registers per
+// lane: the bound makes the compiler fit the absorption's accumulators for
+// 128 sequences within it.
 template <typename ActT, typename WT>
-__global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
+__global__ __launch_bounds__(256, 2) void prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t plds[PREP_LDS / 4];
     const int bid = blockIdx.x;
     if (bid < a.B) {
