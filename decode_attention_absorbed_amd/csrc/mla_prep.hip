@@ -60,9 +60,10 @@ hipError_t launch_rope_freqs(const mla_rope_cfg_t& cfg, float* table, hipStream_
 
 // ---------------------------------------------------------------------------
 // Preparation kernel.  Blocks [0, n_absorb) compute the absorbed content
-// query q_abs = q_nope . W_UK[h] into Q~[b, h, 0:512]; blocks
+// query q_abs = q_nope . W_UK[h] into Q~[b, h, 0:512] and, on the bf16
+// path, the rotary query of their head into Q~[b, h, 512:576]; blocks
 // [n_absorb, n_absorb + B) handle one sequence each: compact the selection
-// and rotate the rotary query into Q~[b, h, 512:576].
+// (and, on the fp32 path, rotate the rotary query).
 // ---------------------------------------------------------------------------
 struct PrepArgs {
     int B, H, K, Lmax, Trope, n_absorb, validate;
@@ -199,6 +200,33 @@ __device__ __forceinline__ void rotate32(const PrepArgs& a, int b, int h, int f0
     }
 }
 
+// Rotary query of 8 pairs (features f .. f + 15) of head h, sequence b, with
+// the table row's (cos, sin) values tv: the bf16 result into
+// Q~[b, h, 512 + f ..] and the remainder (fp32 value minus that bf16 value,
+// rounded to bf16) into the low-part region.
+__device__ __forceinline__ void rotate16_bf16(const PrepArgs& a, int b, int h, int f, const bf16x8 (&xv)[2],
+                                              const f32x4 (&tv)[4]) {
+    bf16x8 v[2], r[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x0 = (float)xv[i >> 2][2 * (i & 3)], x1 = (float)xv[i >> 2][2 * (i & 3) + 1];
+        const float c = tv[i >> 1][2 * (i & 1)], sn = tv[i >> 1][2 * (i & 1) + 1];
+        const float y0 = x0 * c - x1 * sn, y1 = x0 * sn + x1 * c;
+        const bf16 h0 = f2bf(y0), h1 = f2bf(y1);
+        v[i >> 2][2 * (i & 3)] = h0;
+        v[i >> 2][2 * (i & 3) + 1] = h1;
+        r[i >> 2][2 * (i & 3)] = f2bf(y0 - (float)h0);
+        r[i >> 2][2 * (i & 3) + 1] = f2bf(y1 - (float)h1);
+    }
+    bf16* dst = (bf16*)a.qt + ((long long)b * a.H + h) * ROW + RANK + f;
+    bf16* lo = (bf16*)a.qlo + ((long long)b * a.H + h) * D_ROPE + f;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        *(bf16x8*)(dst + 8 * k) = v[k];
+        *(bf16x8*)(lo + 8 * k) = r[k];
+    }
+}
+
 template <typename ActT>
 __device__ __forceinline__ void load_qpe32(const PrepArgs& a, int b, int h, int f0, float (&x)[32]) {
     const ActT* q = (const ActT*)a.q_pe + b * a.qp_sb + h * a.qp_sh + f0;
@@ -221,8 +249,9 @@ __device__ __forceinline__ void load_qpe32(const PrepArgs& a, int b, int h, int 
 
 // One sequence: the selection compaction (every position listed in the
 // index row, minus -1 slots and entries outside [0, L_b), once, ascending)
-// and the rotary query at p_b = L_b - 1 (pairs (2i, 2i+1) are one complex
-// number).  LDS holds a bitmap of ceil(L_b / 32) words, then the compacted
+// and, on the fp32 path, the rotary query at p_b = L_b - 1 (pairs
+// (2i, 2i+1) are one complex number; the bf16 path rotates it in the
+// absorption blocks).  LDS holds a bitmap of ceil(L_b / 32) words, then the compacted
 // list before it is copied out with coalesced stores.  The loads that do
 // not depend on each other (cache length, the first 2048 indices, the first
 // q_pe slices) are issued together; the rotation table row, which needs
@@ -243,8 +272,11 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
         const int j = 4 * tid + 1024 * k;
         iv[k] = j < kv ? *(const int4*)(row + j) : int4{-1, -1, -1, -1};
     }
+    // The bf16 path rotates the query in the absorption blocks (one head
+    // each); the fp32 path does it here.
+    constexpr bool ROT_HERE = sizeof(QtT) == 4;
     float x[32];
-    const bool rot0 = tid < 2 * a.H;                  // this thread's first (head, half)
+    const bool rot0 = ROT_HERE && tid < 2 * a.H;      // this thread's first (head, half)
     if (rot0) load_qpe32<ActT>(a, b, tid >> 1, 32 * (tid & 1), x);
     const int p = min(max(L - 1, 0), a.Trope - 1);
     const float* cs = a.rope_table + (long long)p * D_ROPE;
@@ -329,7 +361,7 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
         if (total == 0) status |= BAD_EMPTY;
     }
     // -- rotary query --
-    for (int e = tid; e < a.H * 2; e += 256) {
+    for (int e = tid; ROT_HERE && e < a.H * 2; e += 256) {
         const int h = e >> 1, f0 = 32 * (e & 1);
         if (e != tid) {
             load_qpe32<ActT>(a, b, h, f0, x);
@@ -441,6 +473,16 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
     const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
 
     const int nrow = min(ABS_QROWS, a.B - b0);
+    // Rotary query of this head's feature half (32 features) for the group's
+    // sequences, worked in while the weight chunks arrive: thread t takes
+    // sequence b0 + t/2, features 32 half + 16 (t & 1) .. +15.  The cache
+    // length is loaded first; q_pe and the table row follow at chunk 3 and
+    // the rotation at chunk 6.
+    const int rs = tid >> 1, rf = 32 * half + 16 * (tid & 1);
+    const bool rot = rs < nrow;
+    const int Lr = rot ? a.cache_lens[b0 + rs] : 1;
+    bf16x8 rxv[2];
+    f32x4 rtv[4];
     {
         // The query copies go out before the weight loads, so the wait for
         // the first weight chunk covers them too.
@@ -471,6 +513,16 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                 asm volatile("" ::: "memory");        // issue chunk c + AHEAD here, not earlier
                 load_chunk(c + ABS_AHEAD);
             }
+            if (c == 3 && rot) {
+                const int p = min(max(Lr - 1, 0), a.Trope - 1);
+                const float* cs = a.rope_table + (long long)p * D_ROPE + rf;
+                const bf16* q = (const bf16*)a.q_pe + (long long)(b0 + rs) * a.qp_sb + h * a.qp_sh + rf;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) rtv[k] = *(const f32x4*)(cs + 4 * k);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) rxv[k] = *(const bf16x8*)(q + 8 * k);
+            }
+            if (c == 6 && rot) rotate16_bf16(a, b0 + rs, h, rf, rxv, rtv);
             // Part pp of the chunk at local rows 16 pp .. 16 pp + 15.  A wave's
             // LDS accesses run in order, so these writes follow the previous
             // chunk's reads.
@@ -569,28 +621,25 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
     }
 }
 
-// Block bid computes absorption slice bid (head bid/2, half bid%2) when
-// bid < 2H, then the selection and rotary query of sequences bid,
-// bid + gridDim.x, ...  The dynamic LDS serves both parts in turn.
-// LDS of a prep block: the absorption's weight staging (4 waves) or the
-// selection bitmap of up to 2^19 positions.  64 KB lets two blocks share a
-// CU, so selection blocks run beside absorption blocks.
+// LDS of a prep block: the absorption's weight staging (4 waves) and query
+// chunk, or the selection bitmap of up to 2^19 positions.  64 KB lets two
+// blocks share a CU, so selection blocks run beside absorption blocks.
 constexpr int PREP_LDS = ABS_Q_OFF + ABS_QROWS * D_NOPE * 2;
 static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 
-// Blocks [0, B) prepare one sequence each (selection, rotary query); blocks
-// [B, B + 2H) compute absorption slice bid - B (head (bid-B)/2, half (bid-B)%2).
-// Two blocks per CU (64 KB of LDS each) need at most 256 registers per
+// Blocks [0, 2H) compute absorption slice bid (head bid/2, half bid%2) and
+// come first, so that each CU gets one of them; blocks [2H, 2H + B) prepare
+// one sequence each.  Two blocks per CU (64 KB of LDS each) need at most 256 registers per
 // lane: the bound makes the compiler fit the absorption's accumulators for
 // 128 sequences within it.
 template <typename ActT, typename WT>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t plds[PREP_LDS / 4];
     const int bid = blockIdx.x;
-    if (bid < a.B) {
-        prep_sequence<ActT, ActT>(a, bid, plds);
+    if (bid >= a.n_absorb) {
+        prep_sequence<ActT, ActT>(a, bid - a.n_absorb, plds);
     } else {
-        const int k = bid - a.B, h = k >> 1, half = k & 1;
+        const int h = bid >> 1, half = bid & 1;
         if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half, (char*)plds);
         else absorb_f32<WT>(a, h, half);
     }
