@@ -106,6 +106,26 @@ def test_small_cases(case):
     _check(dev, out, lse)
 
 
+# More than 128 sequences: the absorption handles sequences 128 at a time
+# (the query chunk in LDS, the accumulators, the rotary query of each
+# group), so these take its later groups, the last one partial, with both
+# weight dtypes.
+BIG_BATCH = [
+    ("b130_h2_f32w", 130, 2, 40, "f32", "random", 0),
+    ("b257_h3_bf16w", 257, 3, 24, "bf16", "alternate", 2),
+]
+
+
+@pytest.mark.parametrize("case", BIG_BATCH, ids=[c[0] for c in BIG_BATCH])
+def test_batch_over_128_sequences(case):
+    name, B, H, K, dw, sel, splits = case
+    lens = np.random.default_rng(B).integers(1, 300, size=B)
+    w = W.build(name, B, H, lens, K, "bf16", dw, W.ROPE_YARN, seed=B + H, selection=sel)
+    dev = Dev(w)
+    out, lse, _ = dev.run(num_splits=splits)
+    _check(dev, out, lse)
+
+
 def _sweep_cases(n=24, seed=2024):
     """Seeded random configurations: head counts around the 32-head wave and
     128-head workgroup boundaries, ragged lengths down to a single row, K not
