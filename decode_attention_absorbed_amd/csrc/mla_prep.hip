@@ -387,9 +387,9 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // split into a bf16 high part and a bf16 remainder, two MFMAs each, so they
 // enter with ~16 significant bits), passed through a wave-private LDS region
 // to be read back transposed (8 consecutive features of one column per
-// lane, ds_read_b64_tr_b16), and multiplied at once into the accumulators
-// of all (up to 128) sequences, so the MFMA work runs under the later
-// chunks' loads.  The queries q_nope[:, h, :] of up to 128 sequences are
+// lane, ds_read_b64_tr_b16), and multiplied into the accumulators of all
+// (up to 128) sequences, so the MFMA work runs under the later chunks'
+// loads; each chunk is staged while the previous one's MFMAs run.  The queries q_nope[:, h, :] of up to 128 sequences are
 // copied into LDS once per block (buffer->LDS, issued before the weight
 // loads) and shared by the 4 waves.
 constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // a wave's staging region (32 of its 64 rows used)
@@ -474,10 +474,10 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
 
     const int nrow = min(ABS_QROWS, a.B - b0);
     // Rotary query of this head's feature half (32 features) for the group's
-    // sequences, worked in while the weight chunks arrive: thread t takes
-    // sequence b0 + t/2, features 32 half + 16 (t & 1) .. +15.  The cache
-    // length is loaded first; q_pe and the table row follow at chunk 3 and
-    // the rotation at chunk 6.
+    // sequences: thread t takes sequence b0 + t/2, features
+    // 32 half + 16 (t & 1) .. +15.  The cache length is loaded first; q_pe
+    // and the table row are loaded after the last weight chunk, land while the
+    // absorbed results are stored, and the rotation follows the stores.
     const int rs = tid >> 1, rf = 32 * half + 16 * (tid & 1);
     const bool rot = rs < nrow;
     const int Lr = rot ? a.cache_lens[b0 + rs] : 1;
@@ -495,9 +495,13 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
         for (int bt = 0; bt < ABS_QROWS / 32; ++bt)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) acc[bt][nb] = f32x16{};
-#pragma unroll
-        for (int c = 0; c < ABS_CHUNKS; ++c) {
-            if (c == 0) wait_vmcnt<4 * (ABS_AHEAD - 1)>();   // query copies and chunk 0 landed
+        // Chunk c's operand: its two bf16 parts (part pp at local rows
+        // 16 pp .. 16 pp + 15 of the wave's LDS region), read back transposed.
+        // Chunk c + AHEAD's loads go out once chunk c has been converted.  A
+        // wave's LDS accesses run in order, so a chunk's writes follow the
+        // previous chunk's reads and its reads follow its writes; the empty
+        // asm statements only keep the compiler from reordering them.
+        auto stage = [&](int c, bf16x8 (&bw)[NP][2]) {
             bf16x4 wp[NP][4];
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
@@ -513,26 +517,12 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                 asm volatile("" ::: "memory");        // issue chunk c + AHEAD here, not earlier
                 load_chunk(c + ABS_AHEAD);
             }
-            if (c == 3 && rot) {
-                const int p = min(max(Lr - 1, 0), a.Trope - 1);
-                const float* cs = a.rope_table + (long long)p * D_ROPE + rf;
-                const bf16* q = (const bf16*)a.q_pe + (long long)(b0 + rs) * a.qp_sb + h * a.qp_sh + rf;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) rtv[k] = *(const f32x4*)(cs + 4 * k);
-#pragma unroll
-                for (int k = 0; k < 2; ++k) rxv[k] = *(const bf16x8*)(q + 8 * k);
-            }
-            if (c == 6 && rot) rotate16_bf16(a, b0 + rs, h, rf, rxv, rtv);
-            // Part pp of the chunk at local rows 16 pp .. 16 pp + 15.  A wave's
-            // LDS accesses run in order, so these writes follow the previous
-            // chunk's reads.
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) *(bf16x4*)(wl + waddr(16 * pp + (lane >> 4) + 4 * ii, cq)) = wp[pp][ii];
-            __builtin_amdgcn_s_waitcnt(0xC07F);       // this wave's writes done (only it reads them)
             asm volatile("" ::: "memory");
-            bf16x8 bw[NP][2];
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
@@ -546,20 +536,52 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                     }
                     bw[pp][nb] = cat(r[0], r[1]);
                 }
-            __builtin_amdgcn_s_waitcnt(0xC07F);       // reads done before the next chunk overwrites
             asm volatile("" ::: "memory");
-            if (c == 0) lds_barrier_only();           // every wave's query copies visible
+        };
+        // Software pipeline: iteration c reads chunk c's query operands, stages
+        // chunk c + 1, then issues chunk c's MFMAs, so the staging's LDS
+        // latency runs under the MFMAs.
+        bf16x8 bwc[NP][2];
+        wait_vmcnt<4 * (ABS_AHEAD - 1)>();            // query copies and chunk 0 landed
+        stage(0, bwc);
+        lds_barrier_only();                           // every wave's query copies visible
+#pragma unroll
+        for (int c = 0; c < ABS_CHUNKS; ++c) {
+            bf16x8 aq[ABS_QROWS / 32];
+#pragma unroll
+            for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+                const int r = 32 * bt + l32;
+                aq[bt] = 32 * bt < nrow ? *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4)) : bf16x8{};
+            }
+            asm volatile("" ::: "memory");
+            bf16x8 bwn[NP][2];
+            if (c + 1 < ABS_CHUNKS) stage(c + 1, bwn);
 #pragma unroll
             for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
                 if (32 * bt < nrow) {
-                    const int r = 32 * bt + l32;
-                    const bf16x8 aq = *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4));
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                        for (int pp = 0; pp < NP; ++pp) acc[bt][nb] = mfma32(bw[pp][nb], aq, acc[bt][nb]);
+                        for (int pp = 0; pp < NP; ++pp) acc[bt][nb] = mfma32(bwc[pp][nb], aq[bt], acc[bt][nb]);
                 }
             }
+            if (c + 1 < ABS_CHUNKS) {
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp)
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) bwc[pp][nb] = bwn[pp][nb];
+            }
+        }
+        // q_pe and the table row for the rotary query, landing while the
+        // results below are stored
+        if (rot) {
+            const int p = min(max(Lr - 1, 0), a.Trope - 1);
+            const float* cs = a.rope_table + (long long)p * D_ROPE + rf;
+            const bf16* q = (const bf16*)a.q_pe + (long long)(b0 + rs) * a.qp_sb + h * a.qp_sh + rf;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) rtv[k] = *(const f32x4*)(cs + 4 * k);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) rxv[k] = *(const bf16x8*)(q + 8 * k);
         }
         // D[column][sequence] (M = 32 columns, N = 32 sequences): lane l holds
         // sequence 32 bt + l%32 and columns 8(i/4) + 4(l/32) + i%4 of block nb.
@@ -593,6 +615,7 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                 asm volatile("" ::: "memory");
             }
         }
+        if (rot) rotate16_bf16(a, b0 + rs, h, rf, rxv, rtv);
     }
 }
 
