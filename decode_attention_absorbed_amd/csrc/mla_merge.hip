@@ -34,7 +34,11 @@ constexpr int MKB = RANK / (16 * MW);   // K steps (16 latent columns) per wave
 
 template <typename WT, typename OutT>
 __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
-    __shared__ float red[MW * 2 * 16 * 64];
+    // Cross-wave reduction buffers, used by alternate batches: a batch's
+    // writes never meet the previous batch's reads, so one barrier per batch
+    // suffices (batch k + 2 reuses batch k's buffer only after every wave has
+    // passed batch k + 1's barrier, i.e. finished batch k's reads).
+    __shared__ float red2[2][MW * 2 * 16 * 64];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     // the two output halves of one head sit 8 ids apart (same XCD, shared L2)
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
                     for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
             if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
                 a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
-            __syncthreads();                        // previous batch's reads of red[] done
+            float* red = red2[(u / G) & 1];
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
