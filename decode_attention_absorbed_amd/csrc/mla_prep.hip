@@ -381,22 +381,22 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // q_abs for head h, latent columns [256*half, 256*half + 256), every
 // sequence, with bf16 MFMA: M = latent columns, N = sequences (32 per
 // step), K = the 128 content features.  Wave w owns 64 columns.  Its
-// weight slice W_UK[h][0:128][64 columns] is read once per 128 sequences
-// with 16-byte loads, in eight chunks of 16 feature rows, two chunks in
-// flight.  Each chunk, as it lands, is converted to bf16 (fp32 weights
-// split into a bf16 high part and a bf16 remainder, two MFMAs each, so they
-// enter with ~16 significant bits), passed through a wave-private LDS region
-// to be read back transposed (8 consecutive features of one column per
-// lane, ds_read_b64_tr_b16), and multiplied into the accumulators of all
-// (up to 128) sequences, so the MFMA work runs under the later chunks'
-// loads; each chunk is staged while the previous one's MFMAs run.  The queries q_nope[:, h, :] of up to 128 sequences are
-// copied into LDS once per block (buffer->LDS, issued before the weight
-// loads) and shared by the 4 waves.
+// weight slice W_UK[h][0:128][64 columns] is read once per group of
+// sequences (128, or 64 when the batch has at most 64) with 16-byte loads,
+// in eight chunks of 16 feature rows, two chunks in flight (four with
+// 64-sequence groups).  Each chunk, as it lands, is converted to bf16 (fp32
+// weights split into a bf16 high part and a bf16 remainder, two MFMAs each,
+// so they enter with ~16 significant bits), passed through a wave-private
+// LDS region to be read back transposed (8 consecutive features of one
+// column per lane, ds_read_b64_tr_b16), and multiplied into the
+// accumulators of every sequence of the group, so the MFMA work runs under
+// the later chunks' loads; each chunk is staged while the previous one's
+// MFMAs run.  The group's queries q_nope[:, h, :] are copied into LDS once
+// (buffer->LDS, issued before the weight loads) and shared by the 4 waves.
 constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // a wave's staging region (32 of its 64 rows used)
-constexpr int ABS_QROWS = 128;                        // sequences per query chunk
+constexpr int ABS_QROWS = 128;                        // sequences per group (query chunk in LDS)
 constexpr int ABS_Q_OFF = 4 * ABS_WAVE_LDS;           // query chunk: [128][128] bf16, 256 B rows
 constexpr int ABS_CHUNKS = D_NOPE / 16;               // weight chunks of 16 feature rows (one K step)
-constexpr int ABS_AHEAD = 2;                          // chunks in flight
 
 // s_barrier after this wave's LDS operations, without waiting for its
 // loads in flight (__syncthreads() waits for those too).
@@ -414,10 +414,13 @@ __device__ __forceinline__ int tid_opaque() {
     return t;
 }
 
-// Sequences [b0, b0 + 128) of head h, latent half `half`.
-template <typename WT>
+// Sequences [b0, b0 + QR) of head h, latent half `half` (QR = 128, or 64
+// when the batch has at most 64 sequences: half the accumulators, which
+// leaves room for four weight chunks in flight instead of two).
+template <typename WT, int QR>
 __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half, char* lds, int b0) {
     constexpr int NP = sizeof(WT) == 4 ? 2 : 1;       // weight parts
+    constexpr int ABS_AHEAD = QR == 64 ? 4 : 2;       // weight chunks in flight
     const int tid = tid_opaque(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, l32 = lane & 31;
     const int c0 = 256 * half + 64 * wave;
@@ -436,14 +439,14 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
     // Copy: instruction i of a wave moves rows 4 (4 wave + i) + l/16, lane l
     // filling slot l % 16, i.e. fetching chunk (l % 16) ^ (row & 15).
     auto copy_q = [&](int b0) {
-        const int nrow = min(ABS_QROWS, a.B - b0);
+        const int nrow = min(QR, a.B - b0);
         const rsrc_t qs = make_rsrc((const bf16*)a.q_nope + b0 * a.qn_sb + h * a.qn_sh,
                                     (uint32_t)((nrow - 1) * a.qn_sb * 2 + D_NOPE * 2));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = 4 * (8 * wave + i) + (lane >> 4);
+        for (int i = 0; i < QR / 16; ++i) {
+            const int r = 4 * (QR / 16 * wave + i) + (lane >> 4);
             const uint32_t off = (uint32_t)(r < nrow ? r * a.qn_sb * 2 : 0x7FFFFFFF) + (uint32_t)((((lane & 15) ^ (r & 15))) << 4);
-            buffer_to_lds16(qs, off, (MLA_LDS void*)(lds + ABS_Q_OFF + (8 * wave + i) * 1024));
+            buffer_to_lds16(qs, off, (MLA_LDS void*)(lds + ABS_Q_OFF + (QR / 16 * wave + i) * 1024));
         }
     };
     // Load: lane l takes columns 4 (l % 16) .. +3 of rows d = l / 16 + 4 i;
@@ -472,7 +475,7 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
     // 32 nb + 16 (blk & 1) + 4 q .. +3.
     const int blk = lane >> 4, L = lane & 15, jj = L >> 2, qq = L & 3;
 
-    const int nrow = min(ABS_QROWS, a.B - b0);
+    const int nrow = min(QR, a.B - b0);
     // Rotary query of this head's feature half (32 features) for the group's
     // sequences: thread t takes sequence b0 + t/2, features
     // 32 half + 16 (t & 1) .. +15.  The cache length is loaded first; q_pe
@@ -490,9 +493,9 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int c = 0; c < ABS_AHEAD; ++c) load_chunk(c);
-        f32x16 acc[ABS_QROWS / 32][2];
+        f32x16 acc[QR / 32][2];
 #pragma unroll
-        for (int bt = 0; bt < ABS_QROWS / 32; ++bt)
+        for (int bt = 0; bt < QR / 32; ++bt)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) acc[bt][nb] = f32x16{};
         // Chunk c's operand: its two bf16 parts (part pp at local rows
@@ -547,9 +550,9 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
         lds_barrier_only();                           // every wave's query copies visible
 #pragma unroll
         for (int c = 0; c < ABS_CHUNKS; ++c) {
-            bf16x8 aq[ABS_QROWS / 32];
+            bf16x8 aq[QR / 32];
 #pragma unroll
-            for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+            for (int bt = 0; bt < QR / 32; ++bt) {
                 const int r = 32 * bt + l32;
                 aq[bt] = 32 * bt < nrow ? *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4)) : bf16x8{};
             }
@@ -557,7 +560,7 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
             bf16x8 bwn[NP][2];
             if (c + 1 < ABS_CHUNKS) stage(c + 1, bwn);
 #pragma unroll
-            for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+            for (int bt = 0; bt < QR / 32; ++bt) {
                 if (32 * bt < nrow) {
 #pragma unroll
                     for (int nb = 0; nb < 2; ++nb)
@@ -589,7 +592,7 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
         // [64 columns] (16-byte chunk k of row r at slot k ^ (r & 7)) and is
         // read back so that 8 lanes write one sequence's 128 contiguous bytes.
 #pragma unroll
-        for (int bt = 0; bt < ABS_QROWS / 32; ++bt) {
+        for (int bt = 0; bt < QR / 32; ++bt) {
             __builtin_amdgcn_sched_barrier(0);
             if (32 * bt < nrow) {
 #pragma unroll
@@ -619,11 +622,11 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
     }
 }
 
-template <typename WT>
+template <typename WT, int QR>
 __device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
-    for (int b0 = 0; b0 < a.B; b0 += ABS_QROWS) {
+    for (int b0 = 0; b0 < a.B; b0 += QR) {
         if (b0 > 0) __syncthreads();                  // every wave done with the previous query chunk
-        absorb_group<WT>(a, h, half, lds, b0);
+        absorb_group<WT, QR>(a, h, half, lds, b0);
     }
 }
 
@@ -655,7 +658,7 @@ static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 // one sequence each.  Two blocks per CU (64 KB of LDS each) need at most 256 registers per
 // lane: the bound makes the compiler fit the absorption's accumulators for
 // 128 sequences within it.
-template <typename ActT, typename WT>
+template <typename ActT, typename WT, int QR>
 __global__ __launch_bounds__(256, 2) void prep_kernel(PrepArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t plds[PREP_LDS / 4];
     const int bid = blockIdx.x;
@@ -663,7 +666,7 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrepArgs a) {
         prep_sequence<ActT, ActT>(a, bid - a.n_absorb, plds);
     } else {
         const int h = bid >> 1, half = bid & 1;
-        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT>(a, h, half, (char*)plds);
+        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT, QR>(a, h, half, (char*)plds);
         else absorb_f32<WT>(a, h, half);
     }
 }
@@ -686,11 +689,14 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     const dim3 grid(a.n_absorb + p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;
     if (plan.bf16_path) {
-        if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prep_kernel<bf16, bf16>), grid, block, 0, s, a);
+        const bool small = p.B <= 64;
+        if (wf && small) hipLaunchKernelGGL((prep_kernel<bf16, float, 64>), grid, block, 0, s, a);
+        else if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float, ABS_QROWS>), grid, block, 0, s, a);
+        else if (small) hipLaunchKernelGGL((prep_kernel<bf16, bf16, 64>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<bf16, bf16, ABS_QROWS>), grid, block, 0, s, a);
     } else {
-        if (wf) hipLaunchKernelGGL((prep_kernel<float, float>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((prep_kernel<float, bf16>), grid, block, 0, s, a);
+        if (wf) hipLaunchKernelGGL((prep_kernel<float, float, ABS_QROWS>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((prep_kernel<float, bf16, ABS_QROWS>), grid, block, 0, s, a);
     }
     return hipGetLastError();
 }
