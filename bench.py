@@ -324,6 +324,94 @@ def bench_op(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_ab(args):
+    """Same-process comparison of builds of the library (--ab LIB [LIB ...]):
+    each build runs the workload's step on the same inputs, with its own
+    workspace and outputs; its output on the first replica is compared with
+    the first build's, then rounds of eager steps alternate the builds'
+    order, and HIP events recorded by each build around its kernels give
+    their mean durations.  Listing one build twice gives the A/A spread.
+    Prints one JSON line."""
+    import numpy as np
+    import torch
+    import workloads as W
+    from decode_attention_absorbed_amd import mla
+
+    torch.cuda.set_device(0)
+    w = W.workload(args.workload)
+    act = torch.bfloat16 if w.dtype_act == "bf16" else torch.float32
+    wt = torch.bfloat16 if w.dtype_w == "bf16" else torch.float32
+    R = 4
+    dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
+    base = dict(q_nope=dev(w.q_nope, act), q_pe=dev(w.q_pe, act), w_uk=dev(w.w_uk, wt), w_uv=dev(w.w_uv, wt),
+                kv_cache=dev(w.kv_cache, act), pe_cache=dev(w.pe_cache, act),
+                topk_indices=torch.from_numpy(w.topk_indices).cuda(),
+                cache_lens=torch.from_numpy(w.cache_lens).cuda())
+    reps = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(R - 1)]
+    table = mla.rope_freqs(w.rope)
+    scale = mla.softmax_scale(192, w.rope)
+    hip = Hip()
+    N = 30                                            # event-timed steps per build per round
+    nk = mla.MLA_NUM_KERNELS
+    events = [[hip.event() for _ in range(2 * nk)] for _ in range(N)]
+    ev_arrays = [(ctypes.c_void_p * len(e))(*[x.value for x in e]) for e in events]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    builds = []
+    for path in args.ab:
+        L = ctypes.CDLL(os.path.abspath(path))
+        L.mla_decode_attn.argtypes = [ctypes.POINTER(mla.DecodeParams), ctypes.c_void_p]
+        L.mla_decode_attn.restype = ctypes.c_int
+        L.mla_decode_workspace_size.argtypes = [ctypes.c_int] * 7
+        L.mla_decode_workspace_size.restype = ctypes.c_size_t
+        n = L.mla_decode_workspace_size(w.B, w.H, w.K, mla._dtype_code(base["kv_cache"]),
+                                        mla._dtype_code(base["w_uk"]), 0, 0)
+        # the buffers live in the build's record for the whole run: params hold raw pointers
+        b = dict(path=path, L=L, ws=torch.empty(n, dtype=torch.uint8, device="cuda"),
+                 out=torch.empty((w.B, w.H, 128), dtype=torch.float32, device="cuda"),
+                 lse=torch.empty((w.B, w.H), dtype=torch.float32, device="cuda"), times=[])
+        b["ps"] = [mla.build_params(r["q_nope"], r["q_pe"], r["w_uk"], r["w_uv"], r["kv_cache"], r["pe_cache"],
+                                    r["topk_indices"], r["cache_lens"], table, scale, b["out"], b["lse"], b["ws"])
+                   for r in reps]
+        builds.append(b)
+
+    def run(b, p):
+        rc = b["L"].mla_decode_attn(ctypes.byref(p), stream)
+        if rc != 0:
+            raise RuntimeError(f"{b['path']}: mla_decode_attn returned {rc}")
+
+    ref = None
+    for b in builds:
+        for i in range(SETTLE_STEPS):
+            run(b, b["ps"][i % R])
+        run(b, b["ps"][0])
+        torch.cuda.synchronize()
+        o = b["out"].clone()
+        ref = o if ref is None else ref
+        b["max_abs_diff_vs_first"] = float((o - ref).abs().max())
+    for rnd in range(args.ab_rounds):
+        for b in (builds if rnd % 2 == 0 else builds[::-1]):
+            for i in range(50):
+                run(b, b["ps"][i % R])
+            for i in range(N):
+                p = b["ps"][i % R]
+                p.profile_events = ctypes.cast(ev_arrays[i], ctypes.c_void_p)
+                run(b, p)
+                p.profile_events = None
+            torch.cuda.synchronize()
+            t = np.array([[hip.elapsed_ms(e[2 * k], e[2 * k + 1]) for k in range(nk)] for e in events]) * 1e3
+            b["times"].append(t.mean(axis=0))
+    res = []
+    for b in builds:
+        t = np.array(b["times"])
+        rec = {"lib": b["path"], "max_abs_diff_vs_first": b["max_abs_diff_vs_first"]}
+        for k, name in enumerate(mla.KERNEL_NAMES):
+            rec[f"{name}_us"] = round(float(t[:, k].mean()), 2)
+            rec[f"{name}_us_min_round"] = round(float(t[:, k].min()), 2)
+        res.append(rec)
+    print(json.dumps({"mode": "ab", "workload": args.workload, "rounds": args.ab_rounds,
+                      "steps_per_round": N, "builds": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,7 +428,17 @@ def main():
     ap.add_argument("--op", default="decode", choices=["decode", "topk", "rope", "append"],
                     help="decode: the decode step (default); others time an adjacent entry point")
     ap.add_argument("--rope-layout", default="halves", choices=["halves", "interleaved"])
+    ap.add_argument("--ab", nargs="+", metavar="LIB",
+                    help="compare builds of libmla_decode.so on the workload's step (same process, "
+                         "alternating order, per-kernel HIP events); one JSON line")
+    ap.add_argument("--ab-rounds", type=int, default=6)
     args = ap.parse_args()
+    if args.ab:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_ab(args)
+        return
     if args.op != "decode":
         if args.gpus != 1:
             print("bench.py measures one GPU only", file=sys.stderr)

@@ -201,7 +201,7 @@ def test_append_host_checks(mla, change, code):
     assert rc == code, mla.last_error()
 
 
-@pytest.mark.parametrize("extra", [[], ["--op", "topk"]])
+@pytest.mark.parametrize("extra", [[], ["--op", "topk"], ["--ab", "x.so", "y.so"]])
 def test_bench_refuses_more_than_one_gpu(extra):
     # one GPU only: the refusal comes before any GPU work
     import subprocess
