@@ -90,6 +90,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(STAGE % 256 == 0 && OFF_Q % 16 == 0, "alignment");
 // Copies per wave per tile: one index fetch, 8 latent rows, one rotary copy.
 constexpr int COPIES_PER_TILE = 10;
+constexpr int Q_EARLY = 16;                          // Q~ register blocks loaded before tile 0's copies
 
 // threadIdx.x through an empty asm statement, read once per pass: values
 // derived from it (lane offsets, addresses) are then computed inside the
@@ -300,6 +301,7 @@ constexpr int QK_AHEAD = 5;
 // query (q^ = hi + lo to 16 significant bits: its rounding to bf16 would
 // otherwise move every score by up to 2^-9 of the rotary term).
 constexpr int NLO = 4;
+constexpr int PRO_LATE = (QK_REG - Q_EARLY) + NLO + COPIES_PER_TILE;   // prologue ops issued after tile 0's copies
 constexpr int NQK = ROW / 16 + NLO;                  // 40 MFMAs
 constexpr int QK_END = 8 + NQK;                      // first step after the chain
 constexpr int NSTEP = 32 + NQK;                      // 72
@@ -480,9 +482,14 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     const rsrc_t qsrc = make_rsrc(a.qt + (long long)sc.b * a.H * ROW, (uint32_t)a.H * ROW * 2u);
     bf16x8 qreg[QK_REG];
     bf16x8 qlo[NLO];
-    if (nt > 0) {
+    {
+        // also for an empty split (nt = 0): its index window reads zeros, so
+        // the copies write zero rows and nothing reads them; a conditional
+        // prologue would make the compiler wait for all its loads where the
+        // two paths join
 #pragma unroll
         for (int T = 0; T < 2; ++T) fetch_idx(sc, T, slot(T), lane, wave);
+        const uint32_t h = (uint32_t)(sc.h0 + wave * 32 + l32);
         {
             // LDS part: lane l fills bytes 16 l of the wave's 1 KB row of
             // block i, i.e. head 32 wave + l/2, features 16 (QK_REG + i) + 8 (l & 1)
@@ -491,24 +498,33 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
             for (int i = 0; i < QK_LDS; ++i)
                 buffer_to_lds16(qsrc, hq * (ROW * 2) + (16 * (QK_REG + i) + 8 * (lane & 1)) * 2,
                                 (MLA_LDS void*)(smem + OFF_Q + 4096 * i + 1024 * wave));
-            const uint32_t h = (uint32_t)(sc.h0 + wave * 32 + l32);
-#pragma unroll
-            for (int ks = 0; ks < QK_REG; ++ks)
-                qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                          qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
-            // low parts of the rotary query: [H][64] per sequence
-            const rsrc_t lsrc = make_rsrc(a.qlo + (long long)sc.b * a.H * D_ROPE, (uint32_t)a.H * D_ROPE * 2u);
-#pragma unroll
-            for (int i = 0; i < NLO; ++i)
-                qlo[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                                        lsrc, h * (D_ROPE * 2) + (16 * i + 8 * g) * 2, 0, 0));
         }
-        wait_vmcnt<QK_LDS + QK_REG + NLO>();       // the two index fetches (issued first) landed
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            fetch_idx(sc, T + 2, slot(T + 2), lane, wave);
-            issue_tile(a, sc, lo, mst, lstage(T), slot(T), lane, wave);
-        }
+        for (int ks = 0; ks < Q_EARLY; ++ks)
+            qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
+        asm volatile("" ::: "memory");
+        wait_vmcnt<QK_LDS + Q_EARLY>();            // the two index fetches (issued first) landed
+        fetch_idx(sc, 2, slot(2), lane, wave);
+        issue_tile(a, sc, lo, mst, lstage(0), slot(0), lane, wave);
+        asm volatile("" ::: "memory");
+        // the rest of Q~ and its low rotary parts load under tile 0's copies
+        // and first MFMA steps (each register block is first used at QK^T
+        // step 8 + its index)
+#pragma unroll
+        for (int ks = Q_EARLY; ks < QK_REG; ++ks)
+            qreg[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                      qsrc, h * (ROW * 2) + (16 * ks + 8 * g) * 2, 0, 0));
+        // low parts of the rotary query: [H][64] per sequence
+        const rsrc_t lsrc = make_rsrc(a.qlo + (long long)sc.b * a.H * D_ROPE, (uint32_t)a.H * D_ROPE * 2u);
+#pragma unroll
+        for (int i = 0; i < NLO; ++i)
+            qlo[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    lsrc, h * (D_ROPE * 2) + (16 * i + 8 * g) * 2, 0, 0));
+        asm volatile("" ::: "memory");
+        fetch_idx(sc, 3, slot(3), lane, wave);
+        issue_tile(a, sc, lo, mst, lstage(1), slot(1), lane, wave);
     }
 
     // ---- main loop ----
@@ -524,7 +540,10 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     }
     const int nrows = sc.end - sc.start;
     for (int it = 0; it < nt; ++it) {
-        wait_vmcnt<COPIES_PER_TILE>();
+        // tile 0: the later Q~ blocks, the low parts and tile 1 may still be
+        // in flight; later tiles: the copies issued during the previous tile
+        if (it == 0) wait_vmcnt<PRO_LATE>();
+        else wait_vmcnt<COPIES_PER_TILE>();
         lds_barrier();          // tile it resident and visible; stage (it-2)%4 free
         const TileRows rows = read_rows(slot(it + 2), lane);
         MLA_LDS char* const dst = lstage(it + 2);
