@@ -13,12 +13,15 @@
 namespace mla {
 
 // ---------------------------------------------------------------------------
-// bf16 path: out[b, h, :] = W_UV[h] . sum_s w_{b,s} o_s[b, h, :]
+// bf16 path: out[b, h, :] = sum_s w_{b,s} (W_UV[h] . o_s[b, h, :])
 //   w_{b,s} = 2^(lse_s - M) / sum_s' 2^(lse_s' - M),  M = max_s lse_s.
-// Workgroup (head h, output half dh) covers every sequence with 8 waves (two
-// per SIMD, so that one wave's loads overlap the other's work).  bf16 MFMA
-// with M = sequences (32 per step), N = 64 outputs, K = 512 latent columns
-// split over the 8 waves (64 each) and reduced through LDS.
+// The projection is linear, so each split's bf16 partial is projected as it
+// is stored (no re-rounding of a merged latent) and the fp32 projections are
+// combined.  Workgroup (head h, output half dh) covers every sequence with 8
+// waves (two per SIMD, so that one wave's loads overlap the other's work).
+// bf16 MFMA with M = 64 outputs (two blocks), N = sequences (32 per step),
+// K = 512 latent columns split over the 8 waves (64 each) and reduced
+// through LDS.
 // ---------------------------------------------------------------------------
 struct MergeArgs {
     int B, H, S;
@@ -36,9 +39,12 @@ template <typename WT, typename OutT>
 __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
     // Cross-wave reduction buffers, used by alternate batches: a batch's
     // writes never meet the previous batch's reads, so one barrier per batch
-    // suffices (batch k + 2 reuses batch k's buffer only after every wave has
-    // passed batch k + 1's barrier, i.e. finished batch k's reads).
-    __shared__ float red2[2][MW * 2 * 16 * 64];
+    // suffices.  Layout [wave][nb][output m][sequence n], rows padded to 33
+    // words: the writes (32 sequences of one output per half-wave) and the
+    // reads (32 consecutive outputs of one sequence) both spread over the banks.
+    constexpr int RS = 33;
+    constexpr int SLAB = 32 * RS;
+    __shared__ float red2[2][MW * 2 * SLAB];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, l32 = lane & 31;
     // the two output halves of one head sit 8 ids apart (same XCD, shared L2)
@@ -96,73 +102,68 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
         }
     }
 
+    // Each split's partial is projected on its own (A = W_UV rows, B = the
+    // partial's latent columns, so a lane's result column is its sequence
+    // and the split weights are per-lane scalars) and the projections are
+    // combined in fp32.  Lanes past the batch hold zero partials and an LSE
+    // of -inf; their columns are never stored.  The last unit of a batch
+    // folds 1 / sum of weights into its coefficients.
     float M = -INFINITY, Wsum = 0.f;
-    float xs[MKB][8];
-#pragma unroll
-    for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
     for (int u = 0; u < U; ++u) {
         if (u + 1 < U) load_unit(u + 1, vn, ln);
-        // fold the current unit's two splits into the running sums
         const float Mn = fmaxf(M, fmaxf(lc[0], lc[1]));
         const float sc = M == Mn ? 1.f : exp2f(M - Mn);
-        const float w0 = exp2f(lc[0] - Mn), w1 = exp2f(lc[1] - Mn);
+        float w0 = exp2f(lc[0] - Mn), w1 = exp2f(lc[1] - Mn);
         Wsum = Wsum * sc + w0 + w1;
-#pragma unroll
-        for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                xs[kb][j] = fmaf(w1, (float)vc[1][kb][j], fmaf(w0, (float)vc[0][kb][j], xs[kb][j] * sc));
         M = Mn;
-        if (u % G == G - 1) {
-            // batch of 32 sequences complete: A operand = merged latent (bf16,
-            // zero past the batch), MFMAs with every lane active, reduction
-            // over the 8 waves' column ranges, output
-            const int b0 = 32 * (u / G), bA = b0 + l32;
+        const bool last = u % G == G - 1;
+        float cs = sc;
+        if (last) {
             const float invW = 1.f / Wsum;
-            bf16x8 av[MKB];
+            cs *= invW; w0 *= invW; w1 *= invW;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            f32x16 p0 = f32x16{}, p1 = f32x16{};
 #pragma unroll
             for (int kb = 0; kb < MKB; ++kb)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) av[kb][j] = bA < a.B ? f2bf(xs[kb][j] * invW) : (bf16)0.f;
-            f32x16 acc[2] = {f32x16{}, f32x16{}};
+                for (int pp = 0; pp < NP; ++pp) {
+                    p0 = mfma32(bw[pp][nb][kb], vc[0][kb], p0);
+                    p1 = mfma32(bw[pp][nb][kb], vc[1][kb], p1);
+                }
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-                for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-                    for (int pp = 0; pp < NP; ++pp) acc[nb] = mfma32(av[kb], bw[pp][nb][kb], acc[nb]);
+            for (int i = 0; i < 16; ++i) acc[nb][i] = fmaf(w1, p1[i], fmaf(w0, p0[i], acc[nb][i] * cs));
+        }
+        if (last) {
+            const int b0 = 32 * (u / G), bA = b0 + l32;
             if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
                 a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
             float* red = red2[(u / G) & 1];
+            // result element (output 8(i/4) + 4g + i%4 of block nb, sequence l32)
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) red[((wave * 2 + nb) * 16 + i) * 64 + lane] = acc[nb][i];
+                for (int i = 0; i < 16; ++i)
+                    red[(wave * 2 + nb) * SLAB + (8 * (i >> 2) + 4 * g + (i & 3)) * RS + l32] = acc[nb][i];
             __syncthreads();
-            // 32 sequences x 64 outputs; D element (row 8(i/4) + 4gg + i%4,
-            // column 32 nb + n) sits at red[w][nb][i][32 gg + n]
 #pragma unroll
             for (int k = 0; k < 2048 / (64 * MW); ++k) {
                 const int e = tid + 64 * MW * k;
                 const int dl = e & 63, bl = e >> 6;
-                const int nb = dl >> 5, n = dl & 31;
-                const int i = 4 * (bl >> 3) + (bl & 3), gg = (bl >> 2) & 1;
-                const int lnn = gg * 32 + n;
+                const int nb = dl >> 5, m = dl & 31;
                 float v = 0.f;
 #pragma unroll
-                for (int w = 0; w < MW; ++w) v += red[((w * 2 + nb) * 16 + i) * 64 + lnn];
+                for (int w = 0; w < MW; ++w) v += red[(w * 2 + nb) * SLAB + m * RS + bl];
                 const int bo = b0 + bl;
                 if (bo < a.B)
                     ((OutT*)a.out)[bo * a.out_sb + h * a.out_sh + 64 * dh + dl] = from_f32<OutT>(v);
             }
             M = -INFINITY;
             Wsum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < MKB; ++kb)
-#pragma unroll
-                for (int j = 0; j < 8; ++j) xs[kb][j] = 0.f;
+            acc[0] = f32x16{};
+            acc[1] = f32x16{};
         }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {

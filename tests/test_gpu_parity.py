@@ -393,10 +393,10 @@ def test_split_count_invariance():
         # Every plan rounds the same probabilities to bf16 (the reference
         # maximum is floored, so moving a split boundary scales them by powers
         # of two only).  What differs is where latent sums are rounded to bf16:
-        # each split's normalised partial, then the merged latent, i.e. two
-        # roundings of at most 2^-9 relative per element in each plan.  Their
-        # difference stays within 4e-3 per output row (about 3.6e-3 at most
-        # on these inputs), well inside the 1e-2 parity bar; a dropped,
+        # each split's normalised partial (at most 2^-9 relative per element;
+        # the merge projects the bf16 partials and combines the projections in
+        # fp32).  Their difference stays within 4e-3 per output row, well
+        # inside the 1e-2 parity bar; a dropped,
         # doubled or misweighted split moves rows by far more.  The log-sum-
         # exp is formed from fp32 sums and agrees to fp32 rounding.
         err = rel_l2_rows(out.cpu().numpy(), base.cpu().numpy()).max()
