@@ -395,13 +395,13 @@ def test_split_count_invariance():
         # of two only).  What differs is where latent sums are rounded to bf16:
         # each split's normalised partial (at most 2^-9 relative per element;
         # the merge projects the bf16 partials and combines the projections in
-        # fp32).  Their difference stays within 4e-3 per output row, well
-        # inside the 1e-2 parity bar; a dropped,
-        # doubled or misweighted split moves rows by far more.  The log-sum-
-        # exp is formed from fp32 sums and agrees to fp32 rounding.
+        # fp32).  Their difference stays within 3.5e-3 per output row (about
+        # 3.1e-3 at most on these inputs), well inside the 1e-2 parity bar;
+        # a dropped, doubled or misweighted split moves rows by far more.  The
+        # log-sum-exp is formed from fp32 sums and agrees to fp32 rounding.
         err = rel_l2_rows(out.cpu().numpy(), base.cpu().numpy()).max()
         print(f"splits {S}: max rel L2 vs one split {err:.3e}", flush=True)
-        assert err <= 4e-3, (S, err)
+        assert err <= 3.5e-3, (S, err)
         assert (lse - base_lse).abs().max().item() <= 1e-5
 
 
