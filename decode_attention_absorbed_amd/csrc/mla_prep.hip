@@ -500,14 +500,17 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
             for (int nb = 0; nb < 2; ++nb) acc[bt][nb] = f32x16{};
         // Chunk c's operand: its two bf16 parts (part pp at local rows
         // 16 pp .. 16 pp + 15 of the wave's LDS region), read back transposed.
-        // Chunk c + AHEAD's loads go out once chunk c has been converted.  A
-        // wave's LDS accesses run in order, so a chunk's writes follow the
-        // previous chunk's reads and its reads follow its writes; the empty
-        // asm statements only keep the compiler from reordering them.
-        auto stage = [&](int c, bf16x8 (&bw)[NP][2]) {
-            bf16x4 wp[NP][4];
+        // The staging of a chunk is four parts: converting feature rows 0-7,
+        // converting rows 8-15 (then chunk c + AHEAD's loads go out), the
+        // LDS writes, the transposed reads.  A wave issues in order, so the
+        // parts of chunk c + 1 are placed between chunk c's MFMA groups (one
+        // group per 32 sequences), where they issue while the matrix core
+        // works.  A wave's LDS accesses run in order, so a chunk's writes
+        // follow the previous chunk's reads and its reads follow its writes.
+        bf16x4 wp[NP][4];
+        auto convert = [&](int c, int half8) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
+            for (int ii = 2 * half8; ii < 2 * half8 + 2; ++ii) {
                 const int i = 4 * c + ii;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -516,16 +519,14 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                     if constexpr (NP == 2) wp[NP - 1][ii][e] = (bf16)(wv[i][e] - (float)hi);
                 }
             }
-            if (c + ABS_AHEAD < ABS_CHUNKS) {
-                asm volatile("" ::: "memory");        // issue chunk c + AHEAD here, not earlier
-                load_chunk(c + ABS_AHEAD);
-            }
-            asm volatile("" ::: "memory");
+        };
+        auto write_stage = [&]() {
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) *(bf16x4*)(wl + waddr(16 * pp + (lane >> 4) + 4 * ii, cq)) = wp[pp][ii];
-            asm volatile("" ::: "memory");
+        };
+        auto read_stage = [&](bf16x8 (&bw)[NP][2]) {
 #pragma unroll
             for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
@@ -539,36 +540,60 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
                     }
                     bw[pp][nb] = cat(r[0], r[1]);
                 }
-            asm volatile("" ::: "memory");
         };
-        // Software pipeline: iteration c reads chunk c's query operands, stages
-        // chunk c + 1, then issues chunk c's MFMAs, so the staging's LDS
-        // latency runs under the MFMAs.
+        // part p of chunk c's staging (c < ABS_CHUNKS)
+        auto stage_part = [&](int c, int p, bf16x8 (&bw)[NP][2]) {
+            if (p == 0) convert(c, 0);
+            if (p == 1) {
+                convert(c, 1);
+                if (c + ABS_AHEAD < ABS_CHUNKS) load_chunk(c + ABS_AHEAD);
+            }
+            if (p == 2) write_stage();
+            if (p == 3) read_stage(bw);
+        };
         bf16x8 bwc[NP][2];
         wait_vmcnt<4 * (ABS_AHEAD - 1)>();            // query copies and chunk 0 landed
-        stage(0, bwc);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            stage_part(0, p, bwc);
+            asm volatile("" ::: "memory");
+        }
         lds_barrier_only();                           // every wave's query copies visible
+        constexpr int NG = QR / 32;                   // MFMA groups per chunk
 #pragma unroll
         for (int c = 0; c < ABS_CHUNKS; ++c) {
-            bf16x8 aq[QR / 32];
+            const bool more = c + 1 < ABS_CHUNKS;
+            // Every group runs, without a branch: query rows past the batch
+            // hold the zeros their out-of-window copies wrote, and their
+            // results are never stored.
+            bf16x8 aq[NG];
 #pragma unroll
-            for (int bt = 0; bt < QR / 32; ++bt) {
+            for (int bt = 0; bt < NG; ++bt) {
                 const int r = 32 * bt + l32;
-                aq[bt] = 32 * bt < nrow ? *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4)) : bf16x8{};
+                aq[bt] = *(const bf16x8*)(ql + r * 256 + (((2 * c + g) ^ (r & 15)) << 4));
             }
-            asm volatile("" ::: "memory");
             bf16x8 bwn[NP][2];
-            if (c + 1 < ABS_CHUNKS) stage(c + 1, bwn);
+            if (NG < 4 && more) stage_part(c + 1, 0, bwn);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int bt = 0; bt < QR / 32; ++bt) {
-                if (32 * bt < nrow) {
+            for (int bt = 0; bt < NG; ++bt) {
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
+                for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-                        for (int pp = 0; pp < NP; ++pp) acc[bt][nb] = mfma32(bwc[pp][nb], aq[bt], acc[bt][nb]);
+                    for (int pp = 0; pp < NP; ++pp) acc[bt][nb] = mfma32(bwc[pp][nb], aq[bt], acc[bt][nb]);
+                if (more) {
+                    // four groups: parts 0, 1 and 2 after groups 0, 1 and 2,
+                    // part 3 after group 2 as well (group 3 then runs under
+                    // the transposed reads' latency); two groups: part 0
+                    // before group 0, part 1 after it, parts 2 and 3 after
+                    // group 1
+#pragma unroll
+                    for (int p = NG >= 4 ? 0 : 1; p < 4; ++p)
+                        if ((NG >= 4 ? (p < 3 ? p : 2) : (p == 1 ? 0 : 1)) == bt) stage_part(c + 1, p, bwn);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            if (c + 1 < ABS_CHUNKS) {
+            if (more) {
 #pragma unroll
                 for (int pp = 0; pp < NP; ++pp)
 #pragma unroll
