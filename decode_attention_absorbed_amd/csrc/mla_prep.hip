@@ -390,9 +390,11 @@ __device__ void prep_sequence(const PrepArgs& a, int b, uint32_t* bm) {
 // LDS region to be read back transposed (8 consecutive features of one
 // column per lane, ds_read_b64_tr_b16), and multiplied into the
 // accumulators of every sequence of the group, so the MFMA work runs under
-// the later chunks' loads; each chunk is staged while the previous one's
-// MFMAs run.  The group's queries q_nope[:, h, :] are copied into LDS once
-// (buffer->LDS, issued before the weight loads) and shared by the 4 waves.
+// the later chunks' loads; the staging of each chunk is split into parts
+// placed between the previous chunk's MFMA groups, where they issue while
+// the matrix core works.  The group's queries q_nope[:, h, :] are copied
+// into LDS once (buffer->LDS, issued before the weight loads) and shared by
+// the 4 waves.
 constexpr int ABS_WAVE_LDS = 64 * 64 * 2;             // a wave's staging region (32 of its 64 rows used)
 constexpr int ABS_QROWS = 128;                        // sequences per group (query chunk in LDS)
 constexpr int ABS_Q_OFF = 4 * ABS_WAVE_LDS;           // query chunk: [128][128] bf16, 256 B rows
