@@ -175,6 +175,203 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Tiled form of the same merge, used for batches of fewer than 128 sequences
+// with at most 8 splits, where it runs faster than the form above (fewer
+// sequence tiles, more split pairs per tile).  The workgroup's 64 W_UV rows (head h,
+// output half dh) go to LDS once, as bf16 high and low parts for fp32
+// weights.  Wave w takes 32-sequence tiles st = w / 2 (+ 4 j) and latent
+// half kh = w % 2, and computes both 32-output blocks of its tile over its
+// 256 columns, with the partial rows streamed from memory MT_PD steps ahead;
+// the two halves of a tile are added through LDS once per tile.  MFMA step
+// ks (0..15), lane group g: latent columns 256 kh + 16 ks + 8 g + j (j < 8),
+// the same for A (W rows, M = outputs) and B (partial rows, N = sequences).
+// LDS holds the weights in operand order, [part][output block][half][step]
+// [lane] x 16 bytes, so each step's read is lane-contiguous.
+// ---------------------------------------------------------------------------
+constexpr int MT_PD = 6;                 // partial steps in flight per wave
+constexpr int MT_XB = 4 * 2 * 16 * 64;   // exchange floats: 4 tiles x 2 blocks x 16 x 64 lanes
+
+template <typename WT, typename OutT>
+__global__ __launch_bounds__(64 * MW) void merge_tile_kernel(MergeArgs a) {
+    constexpr int NP = sizeof(WT) == 4 ? 2 : 1;
+    __shared__ __attribute__((aligned(16))) bf16 wl[NP * 64 * RANK];
+    __shared__ __attribute__((aligned(16))) float xb[MT_XB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, l32 = lane & 31;
+    // the two output halves of one head sit 8 ids apart (same XCD, shared L2)
+    const int id = blockIdx.x;
+    const int xcd = id & 7, k8 = id >> 3;
+    const int dh = k8 & 1, h = (k8 >> 1) * 8 + xcd;
+    if (h >= a.H) return;
+    const int st0 = wave >> 1, kh = wave & 1;
+    const int NST = (a.B + 31) / 32;                 // sequence tiles
+    const int NI = (NST + 3) / 4;                    // tile rounds, the same for every wave
+    const int G = (a.S + 1) / 2;                     // split pairs per sequence
+
+    const rsrc_t prs = make_rsrc(a.opart + (long long)h * a.B * a.S * RANK, (uint32_t)((long long)a.B * a.S * RANK * 2));
+    bf16x8 ring[MT_PD][2];
+    uint32_t voff[2];
+    float lse_n[2];
+    // item (round r, pair gp) of this wave: its first MT_PD steps and two
+    // LSEs.  Lanes past the batch read the last sequence's rows (never
+    // stored); a missing second split reads the last split, LSE -inf.
+    auto issue_item = [&](int r, int gp) {
+        const int bc = min(32 * (st0 + 4 * r) + l32, a.B - 1);
+        const int s0 = 2 * gp, s1 = min(2 * gp + 1, a.S - 1);
+        voff[0] = (uint32_t)(((long long)bc * a.S + s0) * RANK + 256 * kh + 8 * g) * 2u;
+        voff[1] = (uint32_t)(((long long)bc * a.S + s1) * RANK + 256 * kh + 8 * g) * 2u;
+        lse_n[0] = a.lsepart[((long long)h * a.B + bc) * a.S + s0];
+        lse_n[1] = a.lsepart[((long long)h * a.B + bc) * a.S + s1];
+#pragma unroll
+        for (int k = 0; k < MT_PD; ++k)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                ring[k][u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(prs, voff[u] + 32 * k, 0, 0));
+    };
+    const bool has0 = st0 < NST;
+    if (has0) issue_item(0, 0);                      // in flight together with the weights
+
+    // weights: lane = row m (0..63), wave = 16-byte chunks 8 w .. 8 w + 7;
+    // chunk q (columns 8 q .. + 7) is half q / 32, step (q % 32) / 2, group q % 2
+    {
+        const int m = lane, cq = 8 * wave;
+        const WT* wsrc = (const WT*)a.w_uv + h * a.wv_sh + (long long)(64 * dh + m) * RANK + 8 * cq;
+        bf16* dst = wl + 8 * (2048 * (m >> 5) + (m & 31));
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int q = cq + k;
+            const int slot = 1024 * (q >> 5) + 64 * ((q & 31) >> 1) + 32 * (q & 1);
+            if constexpr (NP == 2) {
+                const f32x4 x0 = *(const f32x4*)(wsrc + 8 * k), x1 = *(const f32x4*)(wsrc + 8 * k + 4);
+                bf16x8 hi, lo;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float wv = e < 4 ? x0[e] : x1[e - 4];
+                    hi[e] = (bf16)wv;
+                    lo[e] = (bf16)(wv - (float)hi[e]);
+                }
+                *(bf16x8*)(dst + 8 * slot) = hi;
+                *(bf16x8*)(dst + 64 * RANK + 8 * slot) = lo;
+            } else {
+                *(bf16x8*)(dst + 8 * slot) = load8_bf16<WT>(wsrc + 8 * k);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);              // this wave's LDS writes done
+    asm volatile("s_barrier" ::: "memory");          // every wave's weights visible (loads stay in flight)
+
+    const bool vec_out = ((uintptr_t)a.out & 15) == 0 && (a.out_sb & 3) == 0 && (a.out_sh & 3) == 0;
+    // operand of block ot, part pp, step ks: wop + 8 (4096 pp + 2048 ot + 64 ks)
+    const bf16* wop = wl + 8 * (1024 * kh + lane);
+    float* xw = xb + st0 * (2 * 16 * 64) + lane;     // this tile pair's exchange area
+    for (int r = 0; r < NI; ++r) {
+        const int st = st0 + 4 * r;
+        const bool has = st < NST;
+        float M = -INFINITY, Wsum = 0.f;
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        for (int gp = 0; has && gp < G; ++gp) {
+            const bool last = gp == G - 1;
+            const uint32_t v0 = voff[0], v1 = voff[1];
+            float l0 = lse_n[0], l1 = 2 * gp + 1 < a.S ? lse_n[1] : -INFINITY;
+            f32x16 p[2][2];
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot) { p[ot][0] = f32x16{}; p[ot][1] = f32x16{}; }
+            // weight operands are read one step ahead
+            bf16x8 wc[2][NP];
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) wc[ot][pp] = *(const bf16x8*)(wop + 8 * (4096 * pp + 2048 * ot));
+#pragma unroll
+            for (int ks = 0; ks < 16; ++ks) {
+                bf16x8 wn[2][NP];
+                if (ks + 1 < 16) {
+#pragma unroll
+                    for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                        for (int pp = 0; pp < NP; ++pp)
+                            wn[ot][pp] = *(const bf16x8*)(wop + 8 * (4096 * pp + 2048 * ot + 64 * (ks + 1)));
+                }
+#pragma unroll
+                for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                    for (int pp = 0; pp < NP; ++pp) {
+                        p[ot][0] = mfma32(wc[ot][pp], ring[ks % MT_PD][0], p[ot][0]);
+                        p[ot][1] = mfma32(wc[ot][pp], ring[ks % MT_PD][1], p[ot][1]);
+                    }
+                if (ks + MT_PD < 16) {
+#pragma unroll
+                    for (int u = 0; u < 2; ++u)
+                        ring[ks % MT_PD][u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      prs, (u ? v1 : v0) + 32 * (ks + MT_PD), 0, 0));
+                }
+                if (ks + 1 < 16) {
+#pragma unroll
+                    for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                        for (int pp = 0; pp < NP; ++pp) wc[ot][pp] = wn[ot][pp];
+                }
+                __builtin_amdgcn_sched_barrier(0);   // keep each step's reads with its MFMAs
+            }
+            // the next item streams during the combine
+            if (!last) issue_item(r, gp + 1);
+            else if (st + 4 < NST) issue_item(r + 1, 0);
+            const float Mn = fmaxf(M, fmaxf(l0, l1));
+            const float sc = M == Mn ? 1.f : exp2f(M - Mn);
+            float w0 = exp2f(l0 - Mn), w1 = exp2f(l1 - Mn);
+            Wsum = Wsum * sc + w0 + w1;
+            M = Mn;
+            float cs = sc;
+            if (last) {
+                const float invW = 1.f / Wsum;
+                cs *= invW; w0 *= invW; w1 *= invW;
+            }
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[ot][i] = fmaf(w1, p[ot][1][i], fmaf(w0, p[ot][0][i], acc[ot][i] * cs));
+        }
+        // the upper latent half hands its sums to the lower one
+        if (has && kh == 1) {
+#pragma unroll
+            for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xw[(ot * 16 + i) * 64] = acc[ot][i];
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("s_barrier" ::: "memory");
+        if (has && kh == 0) {
+            // lane: sequence 32 st + l32, outputs 32 ot + 8 i4 + 4 g .. + 3
+            const int bl = 32 * st + l32;
+            if (bl < a.B) {
+                OutT* o = (OutT*)a.out + (long long)bl * a.out_sb + (long long)h * a.out_sh + 64 * dh + 4 * g;
+#pragma unroll
+                for (int ot = 0; ot < 2; ++ot)
+#pragma unroll
+                    for (int i4 = 0; i4 < 4; ++i4) {
+                        float v[4];
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) v[rr] = acc[ot][4 * i4 + rr] + xw[(ot * 16 + 4 * i4 + rr) * 64];
+                        OutT* oo = o + 32 * ot + 8 * i4;
+                        if (vec_out) {
+                            if constexpr (sizeof(OutT) == 4) *(f32x4*)oo = f32x4{v[0], v[1], v[2], v[3]};
+                            else *(bf16x4*)oo = bf16x4{f2bf(v[0]), f2bf(v[1]), f2bf(v[2]), f2bf(v[3])};
+                        } else {
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) oo[rr] = from_f32<OutT>(v[rr]);
+                        }
+                    }
+                if (dh == 0 && g == 0 && a.lse_out) a.lse_out[(long long)bl * a.H + h] = LN2 * (M + log2f(Wsum));
+            }
+        }
+        if (r + 1 < NI) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("s_barrier" ::: "memory");  // exchange area read before the next round writes it
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path.  attn_f32: one workgroup per (sequence, head); scores, softmax
 // and the weighted latent sum in fp32 over the compacted selection, 256 rows
 // at a time with an online rescale between chunks.  Writes the normalised
@@ -285,10 +482,17 @@ hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Wo
     const bool wf = p.dtype_w == MLA_DTYPE_F32, of = p.dtype_out == MLA_DTYPE_F32;
     if (plan.bf16_path) {
         const dim3 grid(((p.H + 7) / 8) * 16), block(64 * MW);
-        if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), grid, block, 0, s, a);
-        else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), grid, block, 0, s, a);
-        else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), grid, block, 0, s, a);
+        if (p.B < 128 && plan.splits <= 8) {
+            if (wf && of) hipLaunchKernelGGL((merge_tile_kernel<float, float>), grid, block, 0, s, a);
+            else if (wf) hipLaunchKernelGGL((merge_tile_kernel<float, bf16>), grid, block, 0, s, a);
+            else if (of) hipLaunchKernelGGL((merge_tile_kernel<bf16, float>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((merge_tile_kernel<bf16, bf16>), grid, block, 0, s, a);
+        } else {
+            if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), grid, block, 0, s, a);
+            else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), grid, block, 0, s, a);
+            else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), grid, block, 0, s, a);
+        }
     } else {
         const long long n = (long long)p.B * p.H * D_V;
         const dim3 grid((unsigned)((n + 255) / 256)), block(256);
