@@ -123,6 +123,20 @@ def test_topk_decode_shape_every_row():
         assert np.array_equal(got[b], want), b
 
 
+def test_topk_narrow_band_large_k():
+    # every score of a row in [1, 1 + 1/16) (one radix digit of sign,
+    # exponent and the leading mantissa bits), ties at many ranks in one row;
+    # selections past 4096 positions (written without LDS staging), rows of
+    # 65536 positions and short rows in the same launch
+    rng = np.random.default_rng(1112)
+    B, L = 3, 65536
+    scores = (1.0 + rng.random((B, L)) / 16.0).astype(np.float32)
+    scores[1, rng.random(L) < 0.2] = np.float32(1.03125)
+    _check(scores, np.array([65536, 20000, 4097]), 5000, "narrow band, k=5000")
+    _check(scores, np.array([65536, 20000, 4097]), 30000, "narrow band, k=30000")
+    _check(scores[:, :16384], np.array([16384, 5000, 4100]), 4096, "narrow band, k=4096")
+
+
 def test_topk_feeds_decode():
     # mla_topk's rows used as the decode step's selection give the oracle's
     # output for the oracle's selection
