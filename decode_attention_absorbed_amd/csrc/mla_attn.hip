@@ -539,22 +539,35 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
         for (int s = 0; s < PV_AHEAD; ++s) ring[s] = pv_operand(smem + stage(NST - 1), t0, t1, 1, s);
     }
     const int nrows = sc.end - sc.start;
-    for (int it = 0; it < nt; ++it) {
-        // tile 0: the later Q~ blocks, the low parts and tile 1 may still be
-        // in flight; later tiles: the copies issued during the previous tile
-        if (it == 0) wait_vmcnt<PRO_LATE>();
-        else wait_vmcnt<COPIES_PER_TILE>();
+    auto tile = [&](int it, bool first) {
         lds_barrier();          // tile it resident and visible; stage (it-2)%4 free
         const TileRows rows = read_rows(slot(it + 2), lane);
         MLA_LDS char* const dst = lstage(it + 2);
         int* const fslot = slot(it + 4);
         tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, qlo, ps, ring, ptail, a.scale_log2,
-                  nrows - it * R, it == 0 && !known, g, [&](int st_) {
+                  nrows - it * R, first, g, [&](int st_) {
             // copies of tile it+2 spread over the tile's 68 MFMA steps
             if (st_ == 1) fetch_idx(sc, it + 4, fslot, lane, wave);
             if (st_ >= 3 && st_ <= 59 && (st_ - 3) % 8 == 0) issue_row(a, sc, lo, dst + mst[(st_ - 3) / 8], rows, (st_ - 3) / 8);
             if (st_ == 63) issue_rot(a, sc, lo, dst, rows, wave);
         });
+    };
+    // Tile 0 is peeled off the loop.  The later Q~ blocks and the low parts
+    // may still be in flight when it starts, so the compiler places a wait
+    // for each register block at its first use; inside a shared loop body
+    // those waits would run on every tile and, late in the QK^T chain, hold
+    // a steady-state tile until the next tile's first copies had landed.
+    // After tile 0 (or the explicit wait of an empty split) no register load
+    // is pending, and the loop below carries only its one copy wait.
+    if (nt > 0) {
+        wait_vmcnt<PRO_LATE>();    // the later Q~ blocks, the low parts and tile 1 may still be in flight
+        tile(0, !known);
+    } else {
+        wait_vmcnt<0>();
+    }
+    for (int it = 1; it < nt; ++it) {
+        wait_vmcnt<COPIES_PER_TILE>();   // the copies issued during the previous tile may be in flight
+        tile(it, false);
     }
     if (nt > 0) pv_last(smem + stage(nt - 1), lo, ps, ring, ptail);
 
