@@ -447,6 +447,44 @@ def test_graph_replay_matches_eager():
         del graph
 
 
+def test_concurrent_streams_match_serial():
+    # Calls on two streams, each with its own workspace, overlap on the device
+    # and still give the outputs of the same calls run one after the other,
+    # bit for bit: a call keeps no state outside its workspace and outputs.
+    rng = np.random.default_rng(41)
+    ws_a = W.build("streams_a", 16, 128, list(rng.integers(1, 6000, 16)), 2048, "bf16", "f32", W.ROPE_YARN,
+                   seed=42)
+    ws_b = W.build("streams_b", 24, 128, list(rng.integers(1, 5000, 24)), 1024, "bf16", "bf16", W.ROPE_YARN,
+                   seed=43)
+    calls = []
+    for dev in (Dev(ws_a), Dev(ws_b)):
+        w = dev.w
+        out = torch.empty((w.B, w.H, 128), dtype=torch.float32, device="cuda")
+        lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+        n = mla.workspace_size(w.B, w.H, w.K, mla._dtype_code(dev.kv), mla._dtype_code(dev.w_uk), 0, 0)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        p = mla.build_params(dev.q_nope, dev.q_pe, dev.w_uk, dev.w_uv, dev.kv, dev.pe, dev.idx, dev.lens,
+                             dev.rope_table, dev.scale, out, lse, ws)
+        calls.append((p, out, lse, ws))
+    for p, *_ in calls:
+        mla.decode_attn(p)
+    torch.cuda.synchronize()
+    refs = [(out.clone(), lse.clone()) for _, out, lse, _ in calls]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        for _, out, lse, ws in calls:
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            ws.fill_(0xFF)
+        torch.cuda.synchronize()
+        for _ in range(4):                  # several calls in flight on each stream
+            for (p, *_), st in zip(calls, streams):
+                mla.decode_attn(p, stream=st)
+        torch.cuda.synchronize()
+        for (_, out, lse, _), (ro, rl) in zip(calls, refs):
+            assert torch.equal(out, ro) and torch.equal(lse, rl), rep
+
+
 def test_fused_buffers_match_separate():
     w = W.build("fused", 3, 128, [300, 900, 50], 200, "bf16", "bf16", W.ROPE_YARN, seed=25)
     dev = Dev(w)
