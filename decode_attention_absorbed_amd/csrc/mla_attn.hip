@@ -27,7 +27,7 @@
 //
 // With one wave per SIMD a wave issues at most one instruction every few
 // cycles, so the tile loop is written to keep its instruction count well
-// under the MFMA time (68 MFMAs of 32 cycles per tile): every LDS operand
+// under the MFMA time (72 MFMAs of 32 cycles per tile): every LDS operand
 // address is a per-lane base plus an immediate offset, the copies of a tile
 // cost the same number of instructions whether its rows exist or not (rows
 // past the split read outside the buffer window and land as zeros), so the
@@ -83,8 +83,6 @@ constexpr int OFF_FLAG = OFF_IDX + NSLOT * 4 * 8 * 4;
 constexpr int QK_REG = 33;                          // Q~ feature blocks 0..32 live in registers,
 constexpr int QK_LDS = ROW / 16 - QK_REG;           // blocks 33..35 in LDS: [block][head][16]
 constexpr int OFF_Q = OFF_FLAG + 16;
-constexpr int QK_DEPTH = 4;                         // QK^T operand reads run this many steps ahead
-constexpr int PV_DEPTH = 4;                         // PV operand reads run this many steps ahead
 constexpr int LDS_BYTES = OFF_Q + QK_LDS * HW * 32;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 static_assert(STAGE % 256 == 0 && OFF_Q % 16 == 0, "alignment");
@@ -230,22 +228,19 @@ __device__ __forceinline__ void qk_settle(f32x16& acc) {
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(acc));
 }
 
-// max(m, x[0..15]) as eight v_max3_f32.  fmaxf on values the compiler
-// cannot prove canonical (results of the inline-asm MFMAs) costs an extra
-// NaN-quieting max per operand.
-__device__ __forceinline__ float max17_raw(float m, const f32x16& x) {
+// max(m, x[o..o+7]) as four v_max3_f32 (two calls cover the 16 entries).
+// fmaxf on values the compiler cannot prove canonical (results of the
+// inline-asm MFMAs) costs an extra NaN-quieting max per operand.
+template <int o>
+__device__ __forceinline__ float max9_raw(float m, const f32x16& x) {
     float r;
     asm("v_max3_f32 %0, %1, %2, %3\n\t"
         "v_max3_f32 %0, %0, %4, %5\n\t"
         "v_max3_f32 %0, %0, %6, %7\n\t"
-        "v_max3_f32 %0, %0, %8, %9\n\t"
-        "v_max3_f32 %0, %0, %10, %11\n\t"
-        "v_max3_f32 %0, %0, %12, %13\n\t"
-        "v_max3_f32 %0, %0, %14, %15\n\t"
-        "v_max3_f32 %0, %0, %16, %17"
+        "v_max3_f32 %0, %0, %8, %9"
         : "=&v"(r)
-        : "v"(m), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
-          "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+        : "v"(m), "v"(x[o]), "v"(x[o + 1]), "v"(x[o + 2]), "v"(x[o + 3]), "v"(x[o + 4]), "v"(x[o + 5]),
+          "v"(x[o + 6]), "v"(x[o + 7]));
     return r;
 }
 
@@ -258,39 +253,43 @@ struct PassState {
     f32x16 o[16];       // [cb]: columns 32cb + 8(i/4) + 4(lane/32) + i%4 of head lane%32
 };
 
-// Probabilities of accumulator entries i and i+1, exponentiated against the
-// reference maximum and added to the running sum; packed into PV B operand
-// pk at e, e+1.  Called one pair per MFMA step so that the transcendental
-// unit never holds up an MFMA issue for long.
-__device__ __forceinline__ void soft2(const f32x16& acc, int i, float m_ref, float scale_log2, float& lsum,
-                                      bf16x8& pk, int e) {
-    const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m_ref));
-    const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i + 1], scale_log2, -m_ref));
+// Probability of accumulator entry i, exponentiated against the reference
+// maximum.  One per MFMA step at most: v_exp_f32 runs at a quarter of the
+// VALU rate, and a step whose other work outlasts its MFMA delays the next
+// one.  Pairs (2j, 2j + 1) are added to the running sum as lsum + (pa + pb)
+// and packed into the PV B operand together.
+__device__ __forceinline__ float soft1(const f32x16& acc, int i, float m_ref, float scale_log2) {
+    return __builtin_amdgcn_exp2f(__builtin_fmaf(acc[i], scale_log2, -m_ref));
+}
+__device__ __forceinline__ void soft_pair(float pa, float pb, float& lsum, bf16x8& pk, int e) {
     lsum += pa + pb;
     pk[e] = f2bf(pa);
     pk[e + 1] = f2bf(pb);
+    asm volatile("" : "+v"(pk));       // pack here, not all four pairs at the first use
 }
 
-// The tile loop's MFMA schedule.  Tile it is one run of 68 steps, one MFMA
+// The tile loop's MFMA schedule.  Tile it is one run of 72 steps, one MFMA
 // each:
 //   steps  0.. 7  PV of tile it-1, K step 1 (its rows 16..31), column blocks 0..7
-//   steps  8..43  QK^T of tile it, feature blocks 0..35
-//   steps 44..51  PV of tile it-1, K step 1, column blocks 8..15
-//   steps 52..67  PV of tile it, K step 0 (rows 0..15), column blocks 0..15
+//   steps  8..47  QK^T of tile it: latent feature blocks 0..31, then the 4
+//                 rotary blocks against the high and the low query parts
+//   steps 48..55  PV of tile it-1, K step 1, column blocks 8..15
+//   steps 56..71  PV of tile it, K step 0 (rows 0..15), column blocks 0..15
 // so that no MFMA waits for the softmax: the probabilities of tile it's rows
-// 0..15 are computed during steps 44..51, which do not need them, and those
-// of rows 16..31 during steps 52..67 (they are used at the next tile's steps
-// 0..7).  The first QK^T operands are read during steps 0..7.  PV: O^T[cb]
-// += V^T(kt, cb) . P^T(kt); the K index k = 8 (lane/32) + e of step kt is
-// row 16kt + 8(e/4) + 4(lane/32) + e%4, matching soft8's operand, and the A
-// operand (columns x those rows) is two transposed reads of 4 rows each.
+// 0..15 are computed during steps 48..55, which do not need them, and those
+// of rows 16..31 during steps 56..71 (they are used at the next tile's steps
+// 0..7 and 48..55).  The copies of tile it+2 are issued during the QK^T
+// chain, whose steps carry only their operand reads.  PV: O^T[cb] +=
+// V^T(kt, cb) . P^T(kt); the K index k = 8 (lane/32) + e of step kt is row
+// 16kt + 8(e/4) + 4(lane/32) + e%4, matching the packed probabilities, and
+// the A operand (columns x those rows) is two transposed reads of 4 rows each.
 // QK^T: S^T[32 rows][32 heads] in acc (lane l: head l%32, rows 8(i/4) +
 // 4(l/32) + i%4 for i = 0..15).
-// PV operands: PV step p (0..31 in a tile: p = s for s < 8, s - 36 for s
-// >= 44) is read PV_AHEAD PV steps earlier into ring slot p % RING (32 =
+// PV operands: PV step p (0..31 in a tile: p = s for s < 8, s - 40 for s
+// >= 48) is read PV_AHEAD PV steps earlier into ring slot p % RING (32 =
 // 8 RING, so the slots line up from tile to tile); the reads for the next
 // tile's PV steps 0..2 (its PV of this tile, K step 1) are issued during
-// steps 65..67.  QK^T operands: feature block ks is read QK_AHEAD steps
+// steps 69..71.  QK^T operands: feature block ks is read QK_AHEAD steps
 // earlier into slot ks % (QK_AHEAD + 1) of a ring that lives within the
 // tile (its first reads are issued during steps 3..7).
 constexpr int RING = 4;
@@ -317,6 +316,12 @@ __host__ __device__ constexpr bool chain_lo(int j) { return j >= 32 && ((j - 32)
 // before it, and no rotary block has a successor KRING blocks later.
 constexpr int KRING = QK_AHEAD + 1;
 static_assert(KRING > QK_AHEAD && KRING >= NLO, "operand ring");
+// Steps after which the copies of tile it+2 are issued: the index fetch of
+// tile it+4, then the 8 latent rows CP_GAP steps apart, then the rotary
+// keys, all within the QK^T chain, whose steps issue little else (the PV
+// steps after it carry the softmax).
+constexpr int CP_IDX = 9, CP_ROW = 11, CP_GAP = 4, CP_ROT = CP_ROW + 8 * CP_GAP;
+static_assert(CP_ROT < QK_END, "copies within the QK^T chain");
 
 // A operand of PV step (kt, cb) of the tile in stage st.
 __device__ __forceinline__ bf16x8 pv_operand(const char* __restrict__ st, int t0, int t1, int kt, int cb) {
@@ -358,6 +363,7 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
     bf16x8 qv[QK_LDS];
     f32x16 acc;
     bf16x8 p0 = {}, p1 = {};
+    float px = 0.f;                    // first entry of the pair being exponentiated
 #pragma clang loop unroll(full)
     for (int s = 0; s < NSTEP; ++s) {
         const bool is_qk = s >= 8 && s < QK_END;
@@ -405,17 +411,33 @@ __device__ __forceinline__ void tile_iter(const char* __restrict__ cur, const ch
                 ps.m_ref = floorf(mt);
             }
         }
-        constexpr int S0 = QK_END, S1 = QK_END + 9;       // softmax of rows 0..15, then 16..31
-        if (s >= S0 && s < S0 + 4) soft2(acc, 2 * (s - S0), ps.m_ref, scale_log2, ps.lsum, p0, 2 * (s - S0));
-        if (s == S0 + 5) ps.mraw = max17_raw(ps.mraw, acc);
-        if (s >= S1 && s < S1 + 4) soft2(acc, 8 + 2 * (s - S1), ps.m_ref, scale_log2, ps.lsum, p1, 2 * (s - S1));
+        // softmax of rows 0..15 one entry per step (steps S0..S0+7, done
+        // before their first PV use at step S0 + 8); rows 16..31 one entry
+        // every other step (S1, S1 + 2, .., S1 + 14), the raw maximum in two
+        // halves between them
+        constexpr int S0 = QK_END, S1 = QK_END + 8;
+        static_assert(S1 + 15 < NSTEP, "softmax steps");
+        if (s >= S0 && s < S0 + 8) {
+            const int j = s - S0;
+            const float x = soft1(acc, j, ps.m_ref, scale_log2);
+            if (j & 1) soft_pair(px, x, ps.lsum, p0, j - 1);
+            else px = x;
+        }
+        if (s >= S1 && s < S1 + 16 && ((s - S1) & 1) == 0) {
+            const int j = (s - S1) >> 1;
+            const float x = soft1(acc, 8 + j, ps.m_ref, scale_log2);
+            if (j & 1) soft_pair(px, x, ps.lsum, p1, j - 1);
+            else px = x;
+        }
+        if (s == S1 + 1) ps.mraw = max9_raw<0>(ps.mraw, acc);
+        if (s == S1 + 3) ps.mraw = max9_raw<8>(ps.mraw, acc);
         hook(s);
         __builtin_amdgcn_sched_barrier(0);
     }
     ptail = p1;
 }
 
-// The last tile's K step 1 (steps 0..7 and 44..51 of a following tile that
+// The last tile's K step 1 (steps 0..7 and 48..55 of a following tile that
 // does not exist).  Its first PV_AHEAD operands are already in the ring.
 __device__ __forceinline__ void pv_last(const char* __restrict__ prv, const LaneOffsets& lo, PassState& ps,
                                         bf16x8 (&ring)[RING], const bf16x8& ptail) {
@@ -467,7 +489,7 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
 #pragma unroll
     for (int cb = 0; cb < 16; ++cb) ps.o[cb] = f32x16{};
 
-    // The first tile's steps 0..7 and 44..51 multiply the stage before stage
+    // The first tile's steps 0..7 and 48..55 multiply the stage before stage
     // 0 (stage NST-1) by zero probabilities: clear its latent region so that
     // whatever it held cannot turn into NaN.
     for (int i = tid; i < LATB / 16; i += 256) *(u32x4*)(smem + (NST - 1) * STAGE + 16 * i) = u32x4{};
@@ -542,14 +564,22 @@ __device__ __forceinline__ bool attn_pass(const AttnArgs& a, const SplitCtx& sc,
     auto tile = [&](int it, bool first) {
         lds_barrier();          // tile it resident and visible; stage (it-2)%4 free
         const TileRows rows = read_rows(slot(it + 2), lane);
-        MLA_LDS char* const dst = lstage(it + 2);
+        const int dsto = stage(it + 2);
         int* const fslot = slot(it + 4);
         tile_iter(smem + stage(it), smem + stage(it + NST - 1), smem, lo, qreg, qlo, ps, ring, ptail, a.scale_log2,
                   nrows - it * R, first, g, [&](int st_) {
-            // copies of tile it+2 spread over the tile's 68 MFMA steps
-            if (st_ == 1) fetch_idx(sc, it + 4, fslot, lane, wave);
-            if (st_ >= 3 && st_ <= 59 && (st_ - 3) % 8 == 0) issue_row(a, sc, lo, dst + mst[(st_ - 3) / 8], rows, (st_ - 3) / 8);
-            if (st_ == 63) issue_rot(a, sc, lo, dst, rows, wave);
+            // copies of tile it+2 spread over the QK^T chain; each copy's LDS
+            // address is formed at its own step (an opaque stage offset), not
+            // all nine at the first one
+            auto dst = [&]() {
+                int o = dsto;
+                asm volatile("" : "+s"(o));
+                return lsm + o;
+            };
+            if (st_ == CP_IDX) fetch_idx(sc, it + 4, fslot, lane, wave);
+            if (st_ >= CP_ROW && st_ < CP_ROW + 8 * CP_GAP && (st_ - CP_ROW) % CP_GAP == 0)
+                issue_row(a, sc, lo, dst() + mst[(st_ - CP_ROW) / CP_GAP], rows, (st_ - CP_ROW) / CP_GAP);
+            if (st_ == CP_ROT) issue_rot(a, sc, lo, dst(), rows, wave);
         });
     };
     // Tile 0 is peeled off the loop.  The later Q~ blocks and the low parts
