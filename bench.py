@@ -38,6 +38,8 @@ DESCR = {
     "long": "B=64, H=128, L=16384, top-k 2048 random incl. newest, bf16",
     "ragged": "B=128, H=128, L_b~U{1024..16384}, top-k=min(2048,L_b) (half random, half recent), "
               "bf16 caches/queries, fp32 W_UK/W_UV",
+    "ragged_h16": "the ragged batch at a 16-head shard: B=128, H=16, L_b~U{1024..16384}, "
+                  "top-k=min(2048,L_b) (half random, half recent), bf16 caches/queries, fp32 W_UK/W_UV",
 }
 
 

@@ -237,7 +237,7 @@ def test_wide_score_spread_f32(mode, c):
 # Full-size workloads, in the launch configuration the bench times, checked
 # on every sequence and head against the oracle.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["batched", "long", "ragged"])
+@pytest.mark.parametrize("name", ["batched", "long", "ragged", "ragged_h16"])
 def test_full_size_every_sequence(name):
     w = W.workload(name)
     dev = Dev(w)

@@ -166,7 +166,7 @@ def new_rows(B: int, dtype_act: str, seed: int):
 
 
 def workload(name: str, batch_limit: int | None = None) -> Workload:
-    """The named workload (tiny, page, batched, long, ragged).  ``batch_limit``
+    """The named workload (tiny, page, batched, long, ragged, ragged_h16).  ``batch_limit``
     draws a smaller batch with the same recipe and seed (its values differ
     from the first sequences of the full batch)."""
     if name == "tiny":
@@ -183,7 +183,13 @@ def workload(name: str, batch_limit: int | None = None) -> Workload:
         B = 128 if batch_limit is None else batch_limit
         return build("ragged", B, 128, None, 2048, "bf16", "f32", ROPE_YARN, 105,
                      L_max=16384, selection="alternate")
+    if name == "ragged_h16":
+        # the ragged batch at a 16-head shard (128 heads over 8 GPUs): the
+        # same recipe with its own seed
+        B = 128 if batch_limit is None else batch_limit
+        return build("ragged_h16", B, 16, None, 2048, "bf16", "f32", ROPE_YARN, 106,
+                     L_max=16384, selection="alternate")
     raise KeyError(name)
 
 
-WORKLOADS = ("tiny", "page", "batched", "long", "ragged")
+WORKLOADS = ("tiny", "page", "batched", "long", "ragged", "ragged_h16")
