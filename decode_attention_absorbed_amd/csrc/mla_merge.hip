@@ -372,10 +372,18 @@ __global__ __launch_bounds__(64 * MW) void merge_tile_kernel(MergeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// fp32 path.  attn_f32: one workgroup per (sequence, head); scores, softmax
-// and the weighted latent sum in fp32 over the compacted selection, 256 rows
-// at a time with an online rescale between chunks.  Writes the normalised
-// latent sum (fp32) and the log2-domain sum-exp.
+// fp32 path (fp32 activations, parity at 1e-5).  attn_f32: one workgroup per
+// (sequence, group of HG heads), 256 threads, over the compacted selection in
+// tiles of 16 rows.  Each tile's rows (latent and rotary parts, 576 floats)
+// are read once into LDS and shared by the group's heads.  The score of
+// (head, row) is formed by TPS = 16 / HG threads, each over a contiguous
+// 576 / TPS features in order, and their partial sums are added with lane
+// shuffles; the threads of a head reduce the tile's maximum and sum the same
+// way (online softmax, rescaling when the maximum grows), and thread tid
+// accumulates latent columns tid and tid + 256 of all HG heads.  Writes the
+// normalised latent sum (fp32) and the log2-domain sum-exp.  HG = 16 reads
+// each row once per 16 heads; HG = 4 runs four times as many workgroups, for
+// batches too small to occupy the chip otherwise.
 // ---------------------------------------------------------------------------
 struct AttnF32Args {
     int B, H, K;
@@ -389,76 +397,187 @@ struct AttnF32Args {
     float* lse2;
 };
 
+constexpr int F32_TR = 16;              // selected rows per tile
+constexpr int F32_RS = ROW + 4;         // LDS row stride (floats): rows 4 banks apart, 16-byte aligned
+constexpr int F32_C4 = ROW / 4;         // 16-byte chunks per row
+
+template <int HG>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
-    __shared__ float qs[ROW];
-    __shared__ float ps[256];
-    __shared__ float wred[4];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = blockIdx.x / a.H, h = blockIdx.x % a.H;
-    const float* q = a.qt + ((long long)b * a.H + h) * ROW;
-    for (int i = tid; i < ROW; i += 256) qs[i] = q[i];
-    __syncthreads();
+    constexpr int TR = F32_TR, TPS = 256 / (HG * TR), CPT = F32_C4 / TPS;
+    static_assert(HG * TR * TPS == 256 && F32_C4 % TPS == 0, "thread mapping");
+    __shared__ __attribute__((aligned(16))) float qs[HG * F32_RS];
+    __shared__ __attribute__((aligned(16))) float ks[TR * F32_RS];
+    __shared__ float ps[HG][TR];
+    __shared__ float al[HG];
+    __shared__ float fin[2][HG];
+    const int tid = threadIdx.x;
+    const int ng = (a.H + HG - 1) / HG;
+    const int b = blockIdx.x / ng, h0 = (blockIdx.x % ng) * HG;
+    const int nh = min(HG, a.H - h0);
+    // Q~ of the group's heads; heads past H are zero (never written out)
+    for (int i = tid; i < HG * F32_C4; i += 256) {
+        const int hh = i / F32_C4, c4 = i % F32_C4;
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (hh < nh) v = *(const f32x4*)(a.qt + ((long long)b * a.H + h0 + hh) * ROW + 4 * c4);
+        *(f32x4*)(qs + hh * F32_RS + 4 * c4) = v;
+    }
     const int cnt = a.counts[b];
     const int32_t* list = a.list + (long long)b * a.K;
-    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int base = 0; base < cnt; base += 256) {
-        const int j = base + tid;
-        float sc = -INFINITY;
-        if (j < cnt) {
-            const long long t = list[j] - 1;   // entries are 1-based
-            const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
-            const float* r = a.pe + b * a.pe_sb + t * a.pe_st;
-            float acc = 0.f;
-            for (int k = 0; k < RANK; ++k) acc = fmaf(qs[k], c[k], acc);
-            for (int k = 0; k < D_ROPE; ++k) acc = fmaf(qs[RANK + k], r[k], acc);
-            sc = acc * a.scale;
+    const float* kvb = a.kv + b * a.kv_sb;
+    const float* peb = a.pe + b * a.pe_sb;
+    // score of head sh, tile row sr, features [CPT q, CPT (q + 1)) in chunks
+    const int q = tid % TPS, sr = (tid / TPS) % TR, sh = tid / (TPS * TR);
+    float m = -INFINITY, l = 0.f;                   // softmax state of head sh (same in all its threads)
+    float o[HG][2];
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) o[hh][0] = o[hh][1] = 0.f;
+    // The tile's rows: 16 x 144 chunks of 16 bytes, 9 per thread.  The next
+    // tile's loads are issued before this tile's scores and stay in flight
+    // (in registers) until the tile after has been consumed.  Rows past the
+    // selection repeat its last row and are stored as zeros: loads without a
+    // condition are not waited for where they are issued.
+    constexpr int NLD = TR * F32_C4 / 256;
+    f32x4 v[NLD];
+    auto fetch = [&](int base) {
+        int t[NLD];
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) t[j] = list[min(base + (tid + 256 * j) / F32_C4, cnt - 1)] - 1;   // 1-based
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int c4 = (tid + 256 * j) % F32_C4;
+            v[j] = c4 < RANK / 4 ? *(const f32x4*)(kvb + (long long)t[j] * a.kv_st + 4 * c4)
+                                 : *(const f32x4*)(peb + (long long)t[j] * a.pe_st + 4 * (c4 - RANK / 4));
         }
-        float cm = wave_max(sc);
-        if (lane == 0) wred[wave] = cm;
+    };
+    if (cnt > 0) fetch(0);
+    for (int base = 0; base < cnt; base += TR) {
+        const int nr = min(TR, cnt - base);
+        __syncthreads();                            // the previous tile's reads of ks, ps, al are done
+#pragma unroll
+        for (int j = 0; j < NLD; ++j) {
+            const int i = tid + 256 * j, r = i / F32_C4, c4 = i % F32_C4;
+            *(f32x4*)(ks + r * F32_RS + 4 * c4) = r < nr ? v[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         __syncthreads();
-        cm = fmaxf(fmaxf(wred[0], wred[1]), fmaxf(wred[2], wred[3]));
-        __syncthreads();
-        const float mn = fmaxf(m, cm);
+        if (base + TR < cnt) fetch(base + TR);
+        float acc = 0.f;
+        const float* qrow = qs + sh * F32_RS + 4 * CPT * q;
+        const float* krow = ks + sr * F32_RS + 4 * CPT * q;
+#pragma unroll 8
+        for (int c4 = 0; c4 < CPT; ++c4) {
+            const f32x4 qv = *(const f32x4*)(qrow + 4 * c4), kv = *(const f32x4*)(krow + 4 * c4);
+            acc = fmaf(qv[0], kv[0], acc);
+            acc = fmaf(qv[1], kv[1], acc);
+            acc = fmaf(qv[2], kv[2], acc);
+            acc = fmaf(qv[3], kv[3], acc);
+        }
+#pragma unroll
+        for (int d = 1; d < TPS; d <<= 1) acc += __shfl_xor(acc, d);
+        const float sc = sr < nr ? acc * a.scale : -INFINITY;
+        float tm = sc;
+#pragma unroll
+        for (int d = TPS; d < TPS * TR; d <<= 1) tm = fmaxf(tm, __shfl_xor(tm, d));
+        const float mn = fmaxf(m, tm);
         const float alpha = m == -INFINITY ? 0.f : expf(m - mn);
-        const float p = j < cnt ? expf(sc - mn) : 0.f;
-        ps[tid] = p;
-        float psum = wave_sum(p);
-        if (lane == 0) wred[wave] = psum;
-        __syncthreads();
-        psum = wred[0] + wred[1] + wred[2] + wred[3];
-        l = l * alpha + psum;
-        o0 *= alpha;
-        o1 *= alpha;
+        const float p = sr < nr ? expf(sc - mn) : 0.f;
+        float ts = p;
+#pragma unroll
+        for (int d = TPS; d < TPS * TR; d <<= 1) ts += __shfl_xor(ts, d);
+        l = l * alpha + ts;
         m = mn;
-        const int nrow = min(256, cnt - base);
-        for (int r = 0; r < nrow; ++r) {
-            const long long t = list[base + r] - 1;
-            const float* c = a.kv + b * a.kv_sb + t * a.kv_st;
-            const float pr = ps[r];
-            o0 = fmaf(pr, c[tid], o0);
-            o1 = fmaf(pr, c[tid + 256], o1);
-        }
+        if (q == 0) ps[sh][sr] = p;
+        if (q == 0 && sr == 0) al[sh] = alpha;
         __syncthreads();
+#pragma unroll
+        for (int hh = 0; hh < HG; ++hh) {
+            const float x = al[hh];
+            o[hh][0] *= x;
+            o[hh][1] *= x;
+        }
+#pragma unroll 4
+        for (int r = 0; r < nr; ++r) {
+            const float v0 = ks[r * F32_RS + tid], v1 = ks[r * F32_RS + tid + 256];
+#pragma unroll
+            for (int hh = 0; hh < HG; ++hh) {
+                const float pr = ps[hh][r];
+                o[hh][0] = fmaf(pr, v0, o[hh][0]);
+                o[hh][1] = fmaf(pr, v1, o[hh][1]);
+            }
+        }
     }
-    const float inv = l > 0.f ? 1.f / l : NAN;
-    float* dst = a.olat + ((long long)b * a.H + h) * RANK;
-    dst[tid] = o0 * inv;
-    dst[tid + 256] = o1 * inv;
-    if (tid == 0) a.lse2[(long long)b * a.H + h] = (m + logf(l)) * LOG2E;
+    if (q == 0 && sr == 0) {
+        fin[0][sh] = l;
+        fin[1][sh] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < HG; ++hh) {
+        if (hh >= nh) break;
+        const float lh = fin[0][hh];
+        const float inv = lh > 0.f ? 1.f / lh : NAN;
+        float* dst = a.olat + ((long long)b * a.H + h0 + hh) * RANK;
+        dst[tid] = o[hh][0] * inv;
+        dst[tid + 256] = o[hh][1] * inv;
+    }
+    if (tid < nh) a.lse2[(long long)b * a.H + h0 + tid] = (fin[1][tid] + logf(fin[0][tid])) * LOG2E;
 }
 
-// fp32 up-projection: one thread per (sequence, head, output feature).
+// fp32 up-projection: one workgroup per (head, half of the 128 outputs,
+// group of 8 sequences) with the group's latent sums in LDS; thread t forms
+// output 64 (half) + t / 4 over latent columns 128 (t % 4) .. + 127 for
+// every sequence of the group, and the four quarters are added with lane
+// shuffles.  Each weight row is read once per group.
+constexpr int F32_UB = 8;               // sequences per up-projection workgroup
+
+template <typename WT>
+__device__ __forceinline__ f32x4 load4_f32(const WT* p);
+template <> __device__ __forceinline__ f32x4 load4_f32<float>(const float* p) { return *(const f32x4*)p; }
+template <> __device__ __forceinline__ f32x4 load4_f32<bf16>(const bf16* p) {
+    const bf16x4 v = *(const bf16x4*)p;
+    return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
 template <typename WT, typename OutT>
 __global__ __launch_bounds__(256) void uproj_f32_kernel(MergeArgs a, const float* olat) {
-    const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (e >= (long long)a.B * a.H * D_V) return;
-    const int d = (int)(e % D_V), h = (int)((e / D_V) % a.H), b = (int)(e / D_V / a.H);
-    const float* x = olat + ((long long)b * a.H + h) * RANK;
-    const WT* w = (const WT*)a.w_uv + h * a.wv_sh + (long long)d * RANK;
-    float acc = 0.f;
-    for (int c = 0; c < RANK; ++c) acc = fmaf(x[c], to_f32(w[c]), acc);
-    ((OutT*)a.out)[b * a.out_sb + h * a.out_sh + d] = from_f32<OutT>(acc);
-    if (d == 0 && a.lse_out) a.lse_out[(long long)b * a.H + h] = a.lsepart[(long long)b * a.H + h] * LN2;
+    __shared__ __attribute__((aligned(16))) float xs[F32_UB][RANK];
+    const int tid = threadIdx.x;
+    const int nbg = (a.B + F32_UB - 1) / F32_UB;
+    const int h = blockIdx.x / (2 * nbg), dh = (blockIdx.x / nbg) & 1, b0 = (blockIdx.x % nbg) * F32_UB;
+    const int nb = min(F32_UB, a.B - b0);
+    for (int i = tid; i < F32_UB * RANK / 4; i += 256) {
+        const int s = i / (RANK / 4), c4 = i % (RANK / 4);
+        f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (s < nb) v = *(const f32x4*)(olat + ((long long)(b0 + s) * a.H + h) * RANK + 4 * c4);
+        *(f32x4*)(xs[s] + 4 * c4) = v;
+    }
+    __syncthreads();
+    const int d = 64 * dh + (tid >> 2), c0 = (RANK / 4) * (tid & 3);
+    const WT* w = (const WT*)a.w_uv + h * a.wv_sh + (long long)d * RANK + c0;
+    float acc[F32_UB];
+#pragma unroll
+    for (int s = 0; s < F32_UB; ++s) acc[s] = 0.f;
+#pragma unroll 16
+    for (int c = 0; c < RANK / 4; c += 4) {
+        const f32x4 wv = load4_f32<WT>(w + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int s = 0; s < F32_UB; ++s) acc[s] = fmaf(xs[s][c0 + c + j], wv[j], acc[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < F32_UB; ++s) {
+        acc[s] += __shfl_xor(acc[s], 1);
+        acc[s] += __shfl_xor(acc[s], 2);
+    }
+    if ((tid & 3) == 0) {
+#pragma unroll
+        for (int s = 0; s < F32_UB; ++s) {
+            if (s >= nb) break;
+            const int bb = b0 + s;
+            ((OutT*)a.out)[bb * a.out_sb + h * a.out_sh + d] = from_f32<OutT>(acc[s]);
+            if (d == 0 && a.lse_out) a.lse_out[(long long)bb * a.H + h] = a.lsepart[(long long)bb * a.H + h] * LN2;
+        }
+    }
 }
 
 hipError_t launch_attn_f32(const mla_decode_params_t& p, const Work& w, hipStream_t s) {
@@ -468,7 +587,10 @@ hipError_t launch_attn_f32(const mla_decode_params_t& p, const Work& w, hipStrea
     a.kv = (const float*)p.kv_cache; a.kv_sb = p.kv_stride_b; a.kv_st = p.kv_stride_t;
     a.pe = (const float*)p.pe_cache; a.pe_sb = p.pe_stride_b; a.pe_st = p.pe_stride_t;
     a.olat = (float*)w.opart; a.lse2 = w.lsepart;
-    hipLaunchKernelGGL(attn_f32_kernel, dim3(p.B * p.H), dim3(256), 0, s, a);
+    // 16 heads per workgroup when that gives enough workgroups, else 4
+    const int g16 = p.B * ((p.H + 15) / 16);
+    if (g16 >= 64) hipLaunchKernelGGL(attn_f32_kernel<16>, dim3(g16), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_f32_kernel<4>, dim3(p.B * ((p.H + 3) / 4)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -494,8 +616,7 @@ hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Wo
             else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), grid, block, 0, s, a);
         }
     } else {
-        const long long n = (long long)p.B * p.H * D_V;
-        const dim3 grid((unsigned)((n + 255) / 256)), block(256);
+        const dim3 grid((unsigned)(p.H * 2 * ((p.B + F32_UB - 1) / F32_UB))), block(256);
         const float* olat = (const float*)w.opart;
         if (wf && of) hipLaunchKernelGGL((uproj_f32_kernel<float, float>), grid, block, 0, s, a, olat);
         else if (wf) hipLaunchKernelGGL((uproj_f32_kernel<float, bf16>), grid, block, 0, s, a, olat);
