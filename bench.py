@@ -414,67 +414,27 @@ def bench_ab(args):
                       "steps_per_round": N, "builds": res}), flush=True)
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="ragged", choices=list(DESCR))
-    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=40.0,
-                    help="seconds of oracle work at most (the ragged batch takes ~10 s on 16 cores)")
-    ap.add_argument("--replicas", type=int, default=0, help="input copies cycled (0 = enough for 1.5 GB)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
-    ap.add_argument("--op", default="decode", choices=["decode", "topk", "rope", "append"],
-                    help="decode: the decode step (default); others time an adjacent entry point")
-    ap.add_argument("--rope-layout", default="halves", choices=["halves", "interleaved"])
-    ap.add_argument("--ab", nargs="+", metavar="LIB",
-                    help="compare builds of libmla_decode.so on the workload's step (same process, "
-                         "alternating order, per-kernel HIP events); one JSON line")
-    ap.add_argument("--ab-rounds", type=int, default=6)
-    args = ap.parse_args()
-    if args.ab:
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
-        bench_ab(args)
-        return
-    if args.op != "decode":
-        if args.gpus != 1:
-            print("bench.py measures one GPU only", file=sys.stderr)
-            sys.exit(2)
-        bench_op(args)
-        return
-    if args.copy_calibration:
-        import torch
-        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}), flush=True)
-        return
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
-              file=sys.stderr)
-        sys.exit(2)
-
+def measure_decode(wname, K, warmup, no_graph=False, replicas=0):
+    """Time the decode step on the named workload: K eager steps with HIP
+    events around each kernel (per-kernel durations), then K steps in a
+    timed region (one HIP-graph replay, or eager launches with no_graph).
+    Returns (line, w, out0, lse0): the JSON fields of the measurement, the
+    workload, and the step's outputs on replica 0 (the workload's own values,
+    taken before any timing) for the parity record."""
     import numpy as np
     import torch
     import workloads as W
     from decode_attention_absorbed_amd import mla
 
     torch.cuda.set_device(0)
-    w = W.workload(args.workload)
+    w = W.workload(wname)
     act = torch.bfloat16 if w.dtype_act == "bf16" else torch.float32
     wt = torch.bfloat16 if w.dtype_w == "bf16" else torch.float32
     rows = w.selected_rows()
     kv_bytes = rows * 576 * (2 if w.dtype_act == "bf16" else 4)
     w_bytes = 2 * w.H * 128 * 512 * (2 if w.dtype_w == "bf16" else 4)
     touched = kv_bytes + w_bytes + w.B * w.H * 192 * 2
-    R = args.replicas or max(2, math.ceil(1.5e9 / touched))
+    R = replicas or max(2, math.ceil(1.5e9 / touched))
 
     dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to(dt).cuda()
     base = dict(q_nope=dev(w.q_nope, act), q_pe=dev(w.q_pe, act), w_uk=dev(w.w_uk, wt), w_uv=dev(w.w_uv, wt),
@@ -491,7 +451,6 @@ def main():
     splits = mla.num_splits(w.B, w.H, w.K, mla._dtype_code(base["kv_cache"]))
 
     hip = Hip()
-    K = args.steps
     events = [[hip.event() for _ in range(2 * mla.MLA_NUM_KERNELS)] for _ in range(K)]
     ev_arrays = [(ctypes.c_void_p * len(e))(*[x.value for x in e]) for e in events]
 
@@ -506,7 +465,7 @@ def main():
     plain = [params(i, False) for i in range(R)]
     timed = [params(i, True) for i in range(K)]
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         mla.decode_attn(plain[i % R])
     torch.cuda.synchronize()
     # Parity snapshot: one step on replica 0 (the workload's own values),
@@ -527,7 +486,7 @@ def main():
     torch.cuda.synchronize()
     eager_ms = None
     graph = None
-    if not args.no_graph:
+    if not no_graph:
         stream = torch.cuda.Stream()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
@@ -576,21 +535,21 @@ def main():
     attn_flops = 2.0 * w.H * (576 + 512) * rows
     flops = attn_flops + 4.0 * w.B * w.H * 128 * 512
     core_s = (per_kernel["attention"] + per_kernel["merge"]) * 1e-3
-    tr = measured_traffic(args.workload)
+    tr = measured_traffic(wname)
     line = {
         "metric": METRIC,
         "value": w.B * K / elapsed,
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype_act == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {DESCR[args.workload]}", "B": w.B, "H": w.H,
+        "config": {"workload": f"{wname}: {DESCR[wname]}", "B": w.B, "H": w.H,
                    "L_max": w.L_max, "top_k": w.K, "selected_rows": rows, "num_splits": splits,
                    "input_replicas": R, "hip_graph": graph is not None},
         "eager_ms_per_step": eager_ms,
@@ -615,10 +574,86 @@ def main():
                      "frac_of_copy": achieved / copy_gbs,
                      "mfma_tflops": 2.0 * w.H * (576 + 512) * rows / t_attn_s / 1e12},
     }
+    return line, w, out0, lse0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="ragged", choices=list(DESCR))
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=40.0,
+                    help="seconds of oracle work at most (the ragged batch takes ~10 s on 16 cores)")
+    ap.add_argument("--replicas", type=int, default=0, help="input copies cycled (0 = enough for 1.5 GB)")
+    ap.add_argument("--also", default=None,
+                    help="comma-separated workloads measured after the primary one into other_workloads "
+                         "(default: long,batched with the ragged workload, none otherwise)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--op", default="decode", choices=["decode", "topk", "rope", "append"],
+                    help="decode: the decode step (default); others time an adjacent entry point")
+    ap.add_argument("--rope-layout", default="halves", choices=["halves", "interleaved"])
+    ap.add_argument("--ab", nargs="+", metavar="LIB",
+                    help="compare builds of libmla_decode.so on the workload's step (same process, "
+                         "alternating order, per-kernel HIP events); one JSON line")
+    ap.add_argument("--ab-rounds", type=int, default=6)
+    args = ap.parse_args()
+    if args.ab:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_ab(args)
+        return
+    if args.op != "decode":
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        bench_op(args)
+        return
+    if args.copy_calibration:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": src.numel() * 4}), flush=True)
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    line, w, out0, lse0 = measure_decode(args.workload, args.steps, args.warmup, args.no_graph, args.replicas)
     if not args.no_cpu_baseline:
         rec, ref, ref_lse = cpu_baseline(w, args.cpu_budget)
         line["cpu_baseline"] = rec
         line["parity"] = parity_record(out0, lse0, ref, ref_lse)
+    # The other full-size workloads, measured the same way in the same run
+    # (outside the metric, which is the primary workload's): a compact
+    # record each, with parity over the rows the oracle finishes.
+    also = args.also.split(",") if args.also is not None else (["long", "batched"] if args.workload == "ragged" else [])
+    others = {}
+    for name in [n for n in also if n and n != "none"]:
+        del w, out0, lse0
+        import torch
+        torch.cuda.empty_cache()
+        ln, w, out0, lse0 = measure_decode(name, args.steps, args.warmup, args.no_graph, args.replicas)
+        keep = ("value", "ms_per_step", "kernel_ms", "attention_frac", "attention_core_frac", "end_to_end_frac",
+                "mfma_pct", "stream_copy_gb_s")
+        rec = {k: ln[k] for k in keep}
+        rec["config"] = ln["config"]
+        rec["roofline"] = {k: ln["roofline"][k] for k in ("achieved", "frac", "traffic", "algorithmic_bytes",
+                                                           "frac_of_copy")}
+        if not args.no_cpu_baseline:
+            _, ref, ref_lse = cpu_baseline(w, args.cpu_budget)
+            rec["parity"] = parity_record(out0, lse0, ref, ref_lse)
+        others[name] = rec
+    if others:
+        line["other_workloads"] = others
     print(json.dumps(line), flush=True)
 
 
