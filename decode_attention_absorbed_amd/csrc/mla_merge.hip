@@ -7,6 +7,8 @@
 //   (x . W_UV[h]^T over the 512 latent columns, 128 outputs per head).
 //   Merging independently normalised partials by their log-sum-exp is the
 //   standard split-softmax identity; the pages do not partition the keys.
+#include <algorithm>
+
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
 
@@ -59,10 +61,18 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
     // finished batch too, so the memory system never idles between batches.
     // Splits are combined with a running maximum (rescaling what was summed
     // when the maximum grows).
+    // With few heads the grid's second dimension splits the 32-sequence
+    // batches between workgroups (each re-reads its weights, from L2 after
+    // the first), so that more CUs share the partials.
     const int G = (a.S + 1) / 2;                     // split pairs per sequence
-    const int U = ((a.B + 31) / 32) * G;
+    const int NBT = (a.B + 31) / 32;                 // 32-sequence batches
+    const int BPG = (NBT + (int)gridDim.y - 1) / (int)gridDim.y;
+    const int bt0 = (int)blockIdx.y * BPG;           // this workgroup's first batch
+    const int nbt = min(BPG, NBT - bt0);
+    if (nbt <= 0) return;
+    const int U = nbt * G;
     auto load_unit = [&](int u, bf16x8 (&v)[2][MKB], float (&ls)[2]) {
-        const int bA = 32 * (u / G) + l32, s0 = 2 * (u % G);
+        const int bA = 32 * (bt0 + u / G) + l32, s0 = 2 * (u % G);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const int s = s0 + t;
@@ -137,7 +147,7 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(MergeArgs a) {
             for (int i = 0; i < 16; ++i) acc[nb][i] = fmaf(w1, p1[i], fmaf(w0, p0[i], acc[nb][i] * cs));
         }
         if (last) {
-            const int b0 = 32 * (u / G), bA = b0 + l32;
+            const int b0 = 32 * (bt0 + u / G), bA = b0 + l32;
             if (dh == 0 && wave == 0 && g == 0 && bA < a.B && a.lse_out)
                 a.lse_out[(long long)bA * a.H + h] = LN2 * (M + log2f(Wsum));
             float* red = red2[(u / G) & 1];
@@ -610,10 +620,13 @@ hipError_t launch_merge(const mla_decode_params_t& p, const Plan& plan, const Wo
             else if (of) hipLaunchKernelGGL((merge_tile_kernel<bf16, float>), grid, block, 0, s, a);
             else hipLaunchKernelGGL((merge_tile_kernel<bf16, bf16>), grid, block, 0, s, a);
         } else {
-            if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), grid, block, 0, s, a);
-            else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), grid, block, 0, s, a);
-            else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), grid, block, 0, s, a);
+            // fewer than 256 workgroups (under 128 heads): split the batches
+            const int nbt = (p.B + 31) / 32;
+            const dim3 gridm(grid.x, (unsigned)std::max(1, std::min(nbt, 256 / (int)grid.x)));
+            if (wf && of) hipLaunchKernelGGL((merge_kernel<float, float>), gridm, block, 0, s, a);
+            else if (wf) hipLaunchKernelGGL((merge_kernel<float, bf16>), gridm, block, 0, s, a);
+            else if (of) hipLaunchKernelGGL((merge_kernel<bf16, float>), gridm, block, 0, s, a);
+            else hipLaunchKernelGGL((merge_kernel<bf16, bf16>), gridm, block, 0, s, a);
         }
     } else {
         const dim3 grid((unsigned)(p.H * 2 * ((p.B + F32_UB - 1) / F32_UB))), block(256);
