@@ -8,6 +8,8 @@
 //                    set per sequence, shared by every head)
 #include <math.h>
 
+#include <algorithm>
+
 #include "mla_device.hpp"
 #include "mla_internal.hpp"
 
@@ -66,7 +68,7 @@ hipError_t launch_rope_freqs(const mla_rope_cfg_t& cfg, float* table, hipStream_
 // (and, on the fp32 path, rotate the rotary query).
 // ---------------------------------------------------------------------------
 struct PrepArgs {
-    int B, H, K, Lmax, Trope, n_absorb, validate;
+    int B, H, K, Lmax, Trope, n_absorb, n_sg, validate;   // n_sg: absorption blocks per head half
     const void* q_nope; long long qn_sb, qn_sh;
     const void* q_pe;   long long qp_sb, qp_sh;
     const void* w_uk;   long long wk_sh;
@@ -649,10 +651,12 @@ __device__ __forceinline__ void absorb_group(const PrepArgs& a, int h, int half,
     }
 }
 
+// Block sg of the head half takes the sequence groups sg, sg + n_sg, ...
+// (n_sg > 1 only with few heads, so that more CUs share the groups).
 template <typename WT, int QR>
-__device__ void absorb_bf16(const PrepArgs& a, int h, int half, char* lds) {
-    for (int b0 = 0; b0 < a.B; b0 += QR) {
-        if (b0 > 0) __syncthreads();                  // every wave done with the previous query chunk
+__device__ void absorb_bf16(const PrepArgs& a, int h, int half, int sg, char* lds) {
+    for (int b0 = sg * QR; b0 < a.B; b0 += a.n_sg * QR) {
+        if (b0 > sg * QR) __syncthreads();            // every wave done with the previous query chunk
         absorb_group<WT, QR>(a, h, half, lds, b0);
     }
 }
@@ -680,9 +684,10 @@ __device__ void absorb_f32(const PrepArgs& a, int h, int half) {
 constexpr int PREP_LDS = ABS_Q_OFF + ABS_QROWS * D_NOPE * 2;
 static_assert(PREP_LDS >= (1 << 19) / 8, "bitmap of the largest cache");
 
-// Blocks [0, 2H) compute absorption slice bid (head bid/2, half bid%2) and
-// come first, so that each CU gets one of them; blocks [2H, 2H + B) prepare
-// one sequence each.  Two blocks per CU (64 KB of LDS each) need at most 256 registers per
+// Blocks [0, n_absorb) compute absorption slices: block bid takes head
+// (bid % 2H) / 2, half bid % 2 and, when n_sg > 1, its share bid / 2H of the
+// sequence groups; they come first, so that each CU gets one of them;
+// blocks [n_absorb, n_absorb + B) prepare one sequence each.  Two blocks per CU (64 KB of LDS each) need at most 256 registers per
 // lane: the bound makes the compiler fit the absorption's accumulators for
 // 128 sequences within it.
 template <typename ActT, typename WT, int QR>
@@ -692,8 +697,9 @@ __global__ __launch_bounds__(256, 2) void prep_kernel(PrepArgs a) {
     if (bid >= a.n_absorb) {
         prep_sequence<ActT, ActT>(a, bid - a.n_absorb, plds);
     } else {
-        const int h = bid >> 1, half = bid & 1;
-        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT, QR>(a, h, half, (char*)plds);
+        const int hb = bid % (2 * a.H), sg = bid / (2 * a.H);
+        const int h = hb >> 1, half = hb & 1;
+        if constexpr (sizeof(ActT) == 2) absorb_bf16<WT, QR>(a, h, half, sg, (char*)plds);
         else absorb_f32<WT>(a, h, half);
     }
 }
@@ -702,7 +708,7 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
                        hipStream_t s) {
     PrepArgs a{};
     a.B = p.B; a.H = p.H; a.K = p.K; a.Lmax = p.max_cache_len; a.Trope = p.rope_table_len;
-    a.n_absorb = 2 * p.H; a.validate = validate ? 1 : 0;
+    a.validate = validate ? 1 : 0;
     a.q_nope = p.q_nope; a.qn_sb = p.q_nope_stride_b; a.qn_sh = p.q_nope_stride_h;
     a.q_pe = p.q_pe; a.qp_sb = p.q_pe_stride_b; a.qp_sh = p.q_pe_stride_h;
     a.w_uk = p.w_uk; a.wk_sh = p.w_uk_stride_h;
@@ -713,10 +719,15 @@ hipError_t launch_prep(const mla_decode_params_t& p, const Plan& plan, const Wor
     a.kv_dst = const_cast<void*>(p.kv_cache); a.kd_sb = p.kv_stride_b; a.kd_st = p.kv_stride_t;
     a.pe_dst = const_cast<void*>(p.pe_cache); a.pd_sb = p.pe_stride_b; a.pd_st = p.pe_stride_t;
     a.qt = w.qt; a.qlo = w.qlo; a.list = w.list; a.counts = w.counts; a.status = w.status;
-    const dim3 grid(a.n_absorb + p.B), block(256);
     const bool wf = p.dtype_w == MLA_DTYPE_F32;
+    // bf16 path: with fewer than 128 heads the 64-sequence groups of one
+    // head half are spread over up to 256 / 2H blocks
+    const int groups64 = (p.B + 63) / 64;
+    a.n_sg = plan.bf16_path && p.H < 128 ? std::max(1, std::min(groups64, 256 / (2 * p.H))) : 1;
+    a.n_absorb = 2 * p.H * a.n_sg;
+    const dim3 grid(a.n_absorb + p.B), block(256);
     if (plan.bf16_path) {
-        const bool small = p.B <= 64;
+        const bool small = p.B <= 64 || a.n_sg > 1;
         if (wf && small) hipLaunchKernelGGL((prep_kernel<bf16, float, 64>), grid, block, 0, s, a);
         else if (wf) hipLaunchKernelGGL((prep_kernel<bf16, float, ABS_QROWS>), grid, block, 0, s, a);
         else if (small) hipLaunchKernelGGL((prep_kernel<bf16, bf16, 64>), grid, block, 0, s, a);
