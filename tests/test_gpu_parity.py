@@ -94,6 +94,9 @@ CASES = [
     # a single head; a single cached row
     ("h1", 3, 1, [40, 300, 1], 64, "bf16", "bf16", "random"),
     ("f32_h1", 2, 1, [1, 77], 16, "f32", "f32", "random"),
+    # fp32 with enough (sequence, 16-head group) pairs for 16-head workgroups,
+    # the last group of each sequence partial
+    ("f32_h20_b40", 40, 20, [37 * (i % 7) + 5 for i in range(40)], 120, "f32", "f32", "random"),
 ]
 
 
