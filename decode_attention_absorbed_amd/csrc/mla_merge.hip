@@ -415,6 +415,7 @@ template <int HG>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnF32Args a) {
     constexpr int TR = F32_TR, TPS = 256 / (HG * TR), CPT = F32_C4 / TPS;
     static_assert(HG * TR * TPS == 256 && F32_C4 % TPS == 0, "thread mapping");
+    static_assert(TPS * TR <= 64, "a head's threads share one wave (its reductions are lane shuffles)");
     __shared__ __attribute__((aligned(16))) float qs[HG * F32_RS];
     __shared__ __attribute__((aligned(16))) float ks[TR * F32_RS];
     __shared__ float ps[HG][TR];
