@@ -450,6 +450,46 @@ def test_graph_replay_matches_eager():
         del graph
 
 
+GRAPH_SMALL = [
+    # below 128 heads: the merge's batch split (second grid dimension) and the
+    # absorption's sequence-group split; the fp32 path's kernels
+    ("graph_h16_b130", 130, 16, 256, "bf16", "f32"),
+    ("graph_f32_h20_b40", 40, 20, 120, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_SMALL, ids=[c[0] for c in GRAPH_SMALL])
+def test_graph_replay_other_launch_shapes(case):
+    # as above, for the launch shapes the 128-head case does not take
+    name, B, H, K, da, dw = case
+    lens = [int(x) for x in np.random.default_rng(B + H).integers(1, 3000, size=B)]
+    w = W.build(name, B, H, lens, K, da, dw, W.ROPE_YARN, seed=B * H)
+    dev = Dev(w)
+    n = mla.workspace_size(w.B, w.H, w.K, mla._dtype_code(dev.kv), mla._dtype_code(dev.w_uk), 0, 0)
+    out = torch.empty((w.B, w.H, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.B, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    p = mla.build_params(dev.q_nope, dev.q_pe, dev.w_uk, dev.w_uv, dev.kv, dev.pe, dev.idx, dev.lens,
+                         dev.rope_table, dev.scale, out, lse, ws)
+    mla.decode_attn(p)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    _check(dev, out, lse, batch=[0, w.B // 2, w.B - 1])
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        mla.decode_attn(p)
+    for r in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        ws.fill_(0xFF)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse), r
+        dev.run()                           # an eager step in between (synchronises)
+    del graph
+
+
 def test_concurrent_streams_match_serial():
     # Calls on two streams, each with its own workspace, overlap on the device
     # and still give the outputs of the same calls run one after the other,
