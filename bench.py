@@ -637,11 +637,15 @@ def main():
     # record each, with parity over the rows the oracle finishes.
     also = args.also.split(",") if args.also is not None else (["long", "batched"] if args.workload == "ragged" else [])
     others = {}
+    del w, out0, lse0
     for name in [n for n in also if n and n != "none"]:
-        del w, out0, lse0
         import torch
         torch.cuda.empty_cache()
-        ln, w, out0, lse0 = measure_decode(name, args.steps, args.warmup, args.no_graph, args.replicas)
+        try:
+            ln, w, out0, lse0 = measure_decode(name, args.steps, args.warmup, args.no_graph, args.replicas)
+        except Exception as e:          # the primary line is printed whatever happens here
+            others[name] = {"error": f"{type(e).__name__}: {e}"}
+            continue
         keep = ("value", "ms_per_step", "kernel_ms", "attention_frac", "attention_core_frac", "end_to_end_frac",
                 "mfma_pct", "stream_copy_gb_s")
         rec = {k: ln[k] for k in keep}
@@ -652,6 +656,7 @@ def main():
             _, ref, ref_lse = cpu_baseline(w, args.cpu_budget)
             rec["parity"] = parity_record(out0, lse0, ref, ref_lse)
         others[name] = rec
+        del w, out0, lse0
     if others:
         line["other_workloads"] = others
     print(json.dumps(line), flush=True)
