@@ -572,6 +572,10 @@ def measure_decode(wname, K, warmup, no_graph=False, replicas=0):
                      "frac": achieved / HBM_PEAK_GBS, "traffic": tr,
                      "kernel": "attention", "algorithmic_bytes": rows * ROW_BYTES_BF16,
                      "frac_of_copy": achieved / copy_gbs,
+                     # all the HBM bytes the counters give per launch (rows, Q~ per split,
+                     # partials) over the same time: how close the kernel runs to the copy rate
+                     "traffic_gb_s": tr / t_attn_s / 1e9 if tr else None,
+                     "traffic_frac_of_copy": tr / t_attn_s / 1e9 / copy_gbs if tr else None,
                      "mfma_tflops": 2.0 * w.H * (576 + 512) * rows / t_attn_s / 1e12},
     }
     return line, w, out0, lse0
@@ -651,7 +655,8 @@ def main():
         rec = {k: ln[k] for k in keep}
         rec["config"] = ln["config"]
         rec["roofline"] = {k: ln["roofline"][k] for k in ("achieved", "frac", "traffic", "algorithmic_bytes",
-                                                           "frac_of_copy")}
+                                                           "frac_of_copy", "traffic_gb_s",
+                                                           "traffic_frac_of_copy")}
         if not args.no_cpu_baseline:
             _, ref, ref_lse = cpu_baseline(w, args.cpu_budget)
             rec["parity"] = parity_record(out0, lse0, ref, ref_lse)
