@@ -19,7 +19,8 @@ namespace mla {
 //   w_{b,s} = 2^(lse_s - M) / sum_s' 2^(lse_s' - M),  M = max_s lse_s.
 // The projection is linear, so each split's bf16 partial is projected as it
 // is stored (no re-rounding of a merged latent) and the fp32 projections are
-// combined.  Workgroup (head h, output half dh) covers every sequence with 8
+// combined.  Workgroup (head h, output half dh) covers every sequence (or,
+// below 128 heads, the 32-sequence batches of its share) with 8
 // waves (two per SIMD, so that one wave's loads overlap the other's work).
 // bf16 MFMA with M = 64 outputs (two blocks), N = sequences (32 per step),
 // K = 512 latent columns split over the 8 waves (64 each) and reduced
